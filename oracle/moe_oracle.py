@@ -1,0 +1,293 @@
+"""Plain CPU oracle for the forward pass of one sparse Mixture-of-Experts layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the GPU library imports, links or calls this
+module, and this module imports nothing from the GPU library.  It may be used by
+``tests/``, by ``__graft_entry__.smoke()`` and by the CPU-baseline leg of ``bench.py``.
+
+Every step is written out as its plain definition in float64 (numpy), with library
+primitives (matmul, a stable sort, erf) as the only building blocks.  No blocking,
+fusion or reordering is applied beyond what the definition states.
+
+Sources (web pages, cited by title/site and section):
+  [mlqm]   www.mlqm.cn/news/130088 (MoE explainer, no title in the extract):
+           §3.1 "Router", §3.3 "Gate", §4.2 "模型定义" (the PyTorch MoE layer code).
+  [rkmt]   "大模型MoE架构揭秘：为什么总参数≠激活参数" (www.rkmt.cn/news/1609753):
+           §2.3 "路由器的设计哲学" (load balance, expert capacity), §3.3 TinyMoE code.
+  [wmrh]   www.wmrh.cn/news/107921 (MoE explainer, no title in the extract):
+           §2.1 gating network, §5.1 toy MoE layer and its printed gate probabilities.
+  [cnnet]  "MoE混合专家架构原理与工程实践：解密大模型稀疏计算真相" (cnnetsun.cn/a/2502649):
+           §3.2 router cost, the DeepSpeed-MoE block.
+  [200B-5] "[从零训练一个200B大语言模型] 5/25：MoE怎样用一部分参数，完成一次计算？"
+           (shanhuang.net): sections "谁来决定请哪几个专家？" (router, top-k, worked
+           combine), "共享专家，给每个token都走的一条路" (shared expert),
+           "200B还在，为什么每次可以少算？" (active-parameter ledger),
+           "四个专家同时算，选两个会更快吗？" (calls per expert).
+
+Readings taken where the pages are silent or disagree (each is pinned by a test in
+tests/test_oracle_pins.py):
+  * selection is made on the fp32 router logits; softmax is monotone, so the top-k of
+    the probabilities equals the top-k of the logits.  Equal logits: lowest expert
+    index first.  Slot j is the j-th best expert.
+  * weights are the softmax probabilities of the selected experts renormalised to sum
+    to 1 ([mlqm] §3.3 and §4.2); temperature is 1.
+  * capacity keeps, per expert, the earliest tokens (ascending token index); an
+    overflowing slot contributes zero and the other weights are not renormalised.
+  * GeLU is the exact erf form; SwiGLU is down(silu(gate x) * (up x)); experts carry no
+    biases; the shared expert is added with weight 1.
+
+Every function here is pinned (see the test module); no function is "parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+from typing import Callable, Dict, Optional, Tuple
+
+import numpy as np
+from scipy.special import erf as _erf
+
+F64 = np.float64
+
+
+# ----------------------------------------------------------------------------------
+# Router: logits, top-k selection, weights
+# ----------------------------------------------------------------------------------
+def router_logits(x: np.ndarray, w_r: np.ndarray, bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """Router logits z = x W_r (+ b), one score per expert.
+
+    [mlqm] §3.1: the router is one linear layer W_r mapping the hidden state h to an
+    E-vector of logits, followed by a softmax.  [rkmt] §3.3 and [wmrh] §5.1 use a linear
+    layer with a bias; the bias here is an optional per-expert offset.
+    The dot products are taken in float64 and the logit is rounded once to fp32, the
+    precision in which the selection is defined.
+    x: [T, d], w_r: [d, E], bias: [E] or None  ->  z: float32 [T, E]
+    """
+    z = np.asarray(x, F64) @ np.asarray(w_r, F64)
+    if bias is not None:
+        z = z + np.asarray(bias, F64)[None, :]
+    return z.astype(np.float32)
+
+
+def expert_order(z: np.ndarray) -> np.ndarray:
+    """Experts of each token ordered by descending logit; equal logits keep ascending
+    expert index (a stable sort of -z).  [200B-5] "谁来决定请哪几个专家？": top-k takes
+    the k highest-scoring candidates."""
+    return np.argsort(-np.asarray(z, F64), axis=1, kind="stable")
+
+
+def select_topk(z: np.ndarray, k: int) -> np.ndarray:
+    """Indices [T, k] of the k best experts per token, best first (int64)."""
+    return expert_order(z)[:, :k].astype(np.int64)
+
+
+def softmax(z: np.ndarray) -> np.ndarray:
+    """Row softmax p_e = exp(z_e) / sum_e' exp(z_e') in float64 ([mlqm] §3.1)."""
+    z64 = np.asarray(z, F64)
+    ez = np.exp(z64 - z64.max(axis=1, keepdims=True))
+    return ez / ez.sum(axis=1, keepdims=True)
+
+
+def topk_weights(z: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """Routing weights w_j = p_{s_j} / sum_i p_{s_i} over the selected experts s.
+
+    [mlqm] §3.3: for top-2, w_i = p_i / (p_i + p_j); [mlqm] §4.2 divides the top-k
+    probabilities by their sum.  Returns float64 [T, k].
+    """
+    p = softmax(z)
+    sel = np.take_along_axis(p, np.asarray(idx, np.int64), axis=1)
+    return sel / sel.sum(axis=1, keepdims=True)
+
+
+def topk_margin(z: np.ndarray, k: int) -> np.ndarray:
+    """z_(k) - z_(k+1): gap between the k-th and (k+1)-th largest logit per token (fp64).
+    Where it is tiny, a different summation order may legitimately flip the selection.
+    +inf when k equals the number of experts."""
+    z64 = np.asarray(z, F64)
+    E = z64.shape[1]
+    if k >= E:
+        return np.full(z64.shape[0], np.inf)
+    s = -np.sort(-z64, axis=1)
+    return s[:, k - 1] - s[:, k]
+
+
+# ----------------------------------------------------------------------------------
+# Capacity and dispatch
+# ----------------------------------------------------------------------------------
+def capacity_rule(T: int, k: int, E: int, factor: float = 1.0) -> int:
+    """Per-expert capacity C = factor * T * k / E, rounded up.
+
+    [rkmt] §2.3: with 1024 tokens, K=2 and 16 experts the capacity is (1024x2)/16 = 128.
+    The page's example divides exactly; for a non-integral quotient the ceiling is taken
+    so that a perfectly balanced load never drops a token.
+    """
+    return int(math.ceil(factor * T * k / E))
+
+
+def dispatch(idx: np.ndarray, E: int, capacity: int = 0) -> Dict[str, np.ndarray]:
+    """Group token slots by expert, apply the capacity, build the permutation.
+
+    [rkmt] §2.3: each expert takes at most C tokens; the rest are dropped.  The earliest
+    tokens (ascending token index) are the ones kept.  [200B-5] "四个专家同时算…": every
+    selection is one call of one expert, so sum(counts) = T*k.
+
+    idx: [T, k] expert per slot.  capacity <= 0 means no limit.
+    Returns
+      counts  [E]    number of slots that selected each expert (demand)
+      kept    [E]    min(counts, C)
+      offsets [E+1]  exclusive prefix sum of kept
+      perm    [R]    row r of the expert-sorted order holds slot t*k+j; rows of one
+                     expert are in ascending token order
+      inv     [T,k]  row of slot (t, j), or -1 if the slot was dropped
+      n_dropped      number of dropped slots
+    """
+    idx = np.asarray(idx, np.int64)
+    T, k = idx.shape
+    counts = np.zeros(E, np.int64)
+    arrival = np.zeros((T, k), np.int64)
+    for t in range(T):
+        for j in range(k):
+            e = int(idx[t, j])
+            arrival[t, j] = counts[e]
+            counts[e] += 1
+    if capacity > 0:
+        keep = arrival < capacity
+        kept = np.minimum(counts, capacity)
+    else:
+        keep = np.ones((T, k), bool)
+        kept = counts.copy()
+    offsets = np.zeros(E + 1, np.int64)
+    offsets[1:] = np.cumsum(kept)
+    perm = np.empty(int(offsets[-1]), np.int64)
+    inv = np.full((T, k), -1, np.int64)
+    for t in range(T):
+        for j in range(k):
+            if keep[t, j]:
+                e = int(idx[t, j])
+                r = int(offsets[e] + arrival[t, j])
+                perm[r] = t * k + j
+                inv[t, j] = r
+    return dict(counts=counts, kept=kept, offsets=offsets, perm=perm, inv=inv,
+                n_dropped=int((~keep).sum()))
+
+
+# ----------------------------------------------------------------------------------
+# Expert FFN and combine
+# ----------------------------------------------------------------------------------
+def gelu(v: np.ndarray) -> np.ndarray:
+    """Exact GeLU v * Phi(v) = 0.5 v (1 + erf(v / sqrt 2)) ([cnnet] and [rkmt] §3.3 use nn.GELU)."""
+    v = np.asarray(v, F64)
+    return 0.5 * v * (1.0 + _erf(v / math.sqrt(2.0)))
+
+
+def silu(v: np.ndarray) -> np.ndarray:
+    """SiLU v * sigmoid(v) = v / (1 + exp(-v))."""
+    v = np.asarray(v, F64)
+    with np.errstate(over="ignore"):
+        return v / (1.0 + np.exp(-v))
+
+
+def expert_ffn(xr: np.ndarray, act: str, w_gate: np.ndarray, w_up: Optional[np.ndarray],
+               w_down: np.ndarray) -> np.ndarray:
+    """One expert applied to the rows xr [n, d] (weights in nn.Linear layout, [out, in]).
+
+    GeLU expert ([cnnet] DeepSpeed block, [rkmt] §3.3): y = W2 gelu(W1 x),
+        w_gate = W1 [F, d], w_down = W2 [d, F], w_up unused.
+    SwiGLU expert ([mlqm] §3.2 names SwiGLU): y = Wd (silu(Wg x) * (Wu x)),
+        w_gate = Wg [F, d], w_up = Wu [F, d], w_down = Wd [d, F].
+    """
+    xr = np.asarray(xr, F64)
+    g = xr @ np.asarray(w_gate, F64).T
+    if act == "gelu":
+        h = gelu(g)
+    elif act == "swiglu":
+        h = silu(g) * (xr @ np.asarray(w_up, F64).T)
+    else:
+        raise ValueError(act)
+    return h @ np.asarray(w_down, F64).T
+
+
+def combine(y_slots: np.ndarray, w: np.ndarray, keep: Optional[np.ndarray] = None,
+            shared: Optional[np.ndarray] = None) -> np.ndarray:
+    """out[t] = sum_j keep[t,j] * w[t,j] * y_slots[t,j] (+ shared[t]).
+
+    [200B-5] "谁来决定请哪几个专家？": the selected experts' output vectors are mixed in
+    proportion to the routing weights (0.75 x E1 + 0.25 x E3 in the worked example).
+    [200B-5] "共享专家…": the shared expert's result is added to the routed result.
+    y_slots: [T, k, d], w: [T, k], keep: [T, k] bool or None, shared: [T, d] or None.
+    """
+    y_slots = np.asarray(y_slots, F64)
+    w = np.asarray(w, F64)
+    if keep is not None:
+        w = np.where(np.asarray(keep, bool), w, 0.0)
+    out = np.einsum("tk,tkd->td", w, y_slots)
+    if shared is not None:
+        out = out + np.asarray(shared, F64)
+    return out
+
+
+ExpertWeights = Tuple[np.ndarray, Optional[np.ndarray], np.ndarray]
+
+
+def routed_output(x_rows: np.ndarray, idx_rows: np.ndarray, w_rows: np.ndarray,
+                  keep_rows: np.ndarray, act: str,
+                  expert_weights: Callable[[int], ExpertWeights],
+                  shared_weights: Optional[ExpertWeights] = None) -> np.ndarray:
+    """Layer output for some tokens, given their routing (teacher-forced FFN + combine).
+
+    x_rows [n, d]; idx_rows, w_rows, keep_rows [n, k].  expert_weights(e) returns
+    (w_gate, w_up, w_down) of routed expert e; shared_weights those of the shared expert.
+    Each expert is evaluated on the rows that selected it and kept the slot.
+    """
+    x_rows = np.asarray(x_rows, F64)
+    n, k = idx_rows.shape
+    y_slots = np.zeros((n, k, x_rows.shape[1]), F64)
+    for e in np.unique(idx_rows[keep_rows]):
+        sel = (idx_rows == e) & keep_rows
+        tok, slot = np.nonzero(sel)
+        y_slots[tok, slot] = expert_ffn(x_rows[tok], act, *expert_weights(int(e)))
+    shared = None
+    if shared_weights is not None:
+        shared = expert_ffn(x_rows, act, *shared_weights)
+    return combine(y_slots, w_rows, keep_rows, shared)
+
+
+def moe_layer(x: np.ndarray, w_r: np.ndarray, k: int, act: str,
+              w_gate: np.ndarray, w_up: Optional[np.ndarray], w_down: np.ndarray,
+              bias: Optional[np.ndarray] = None, capacity: int = 0,
+              shared: Optional[ExpertWeights] = None) -> Dict[str, np.ndarray]:
+    """Whole layer: router -> top-k -> weights -> capacity/dispatch -> experts -> combine.
+
+    Follows [mlqm] §3.1-§3.3 and §4.2, [rkmt] §2.3 and [200B-5].  Stacked expert weights:
+    w_gate [E, F, d], w_up [E, F, d] or None, w_down [E, d, F].
+    Returns the float64 output [T, d] (unrounded) and every intermediate.
+    """
+    E = np.asarray(w_r).shape[1]
+    z = router_logits(x, w_r, bias)
+    idx = select_topk(z, k)
+    w = topk_weights(z, idx)
+    disp = dispatch(idx, E, capacity)
+    keep = disp["inv"] >= 0
+    out = routed_output(
+        x, idx, w, keep, act,
+        lambda e: (w_gate[e], None if w_up is None else w_up[e], w_down[e]),
+        shared)
+    res = dict(out=out, logits=z, idx=idx, w=w, margin=topk_margin(z, k))
+    res.update(disp)
+    return res
+
+
+# ----------------------------------------------------------------------------------
+# Ledgers
+# ----------------------------------------------------------------------------------
+def active_params(common: float, routed_total: float, E: int, k: int) -> float:
+    """Parameters one token passes through: common + routed_total * k / E.
+
+    [200B-5] "200B还在，为什么每次可以少算？": 40B common + 160B routed over 16 experts,
+    2 selected -> 160B x 2 / 16 + 40B = 60B.
+    """
+    return common + routed_total * k / E
+
+
+def expert_weight_bytes(E: int, d: int, F: int, act: str, bytes_per_elem: int) -> int:
+    """Bytes of E stacked experts: 3 d F weights each for SwiGLU, 2 d F for GeLU."""
+    mats = 3 if act == "swiglu" else 2
+    return E * mats * d * F * bytes_per_elem

@@ -1,0 +1,412 @@
+"""Pins of the CPU oracle against what the source pages and the mathematics fix.
+
+Each ``check_*`` function is one pin; the ``test_*`` functions run them against the
+oracle as it stands, and ``test_mutation_*`` plant a plausible mistake in the oracle
+(on the CPU, through monkeypatch) and require that some pin catches it.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as Fnn
+
+from oracle import moe_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name), encoding="utf-8") as f:
+        return json.load(f)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------------------------
+# torch (CPU, float64) textbook forms used as independent references
+# ---------------------------------------------------------------------------------
+def _torch_ffn(x, act, wg, wu, wd):
+    x = torch.as_tensor(np.asarray(x, np.float64))
+    wg = torch.as_tensor(np.asarray(wg, np.float64))
+    wd = torch.as_tensor(np.asarray(wd, np.float64))
+    if act == "gelu":
+        h = Fnn.gelu(Fnn.linear(x, wg))
+    else:
+        wu = torch.as_tensor(np.asarray(wu, np.float64))
+        h = Fnn.silu(Fnn.linear(x, wg)) * Fnn.linear(x, wu)
+    return Fnn.linear(h, wd).numpy()
+
+
+def _rand_experts(rng, E, d, F, act):
+    wg = rng.standard_normal((E, F, d)) / math.sqrt(d)
+    wu = rng.standard_normal((E, F, d)) / math.sqrt(d) if act == "swiglu" else None
+    wd = rng.standard_normal((E, d, F)) / math.sqrt(F)
+    return wg, wu, wd
+
+
+# ---------------------------------------------------------------------------------
+# Pins
+# ---------------------------------------------------------------------------------
+def check_worked_combine():
+    g = _golden("worked_combine.json")
+    y = np.array([g["expert_outputs"]])            # [1, k=2, d=3]
+    w = np.array([g["weights"]])
+    out = O.combine(y, w)[0]
+    np.testing.assert_allclose(out, g["mixture"], rtol=0, atol=1e-15)
+    assert abs(out[0] - (0.75 * 0.8 + 0.25 * 0.4)) < 1e-15
+
+
+def _worked_layer(act):
+    """E=4, d=3: token x = e_0; the router puts logit ln 3 on E1 and 0 on E3 (others far
+    below), so the renormalised weights are 3/4 and 1/4.  Each expert has F=1 and is
+    built so that it returns a prescribed vector for this token."""
+    g = _golden("worked_combine.json")
+    targets = np.array([g["expert_outputs"][0], [9.0, 9.0, 9.0],
+                        g["expert_outputs"][1], [-9.0, 9.0, -9.0]])
+    d, E, F = 3, 4, 1
+    x = np.array([[1.0, 0.0, 0.0]])
+    w_r = np.zeros((d, E))
+    w_r[0] = [math.log(3.0), -10.0, 0.0, -10.0]
+    a = 1.0
+    wg = np.zeros((E, F, d))
+    wg[:, 0, 0] = a
+    if act == "swiglu":
+        wu = np.zeros((E, F, d))
+        wu[:, 0, 0] = 1.0
+        hval = O.silu(np.array(a))
+    else:
+        wu = None
+        hval = O.gelu(np.array(a))
+    wd = targets[:, :, None] / hval                  # [E, d, F]
+    return O.moe_layer(x, w_r, 2, act, wg, wu, wd), g
+
+
+def check_worked_layer():
+    for act in ("swiglu", "gelu"):
+        res, g = _worked_layer(act)
+        assert list(res["idx"][0]) == g["chosen"]
+        np.testing.assert_allclose(res["w"][0], g["weights"], rtol=0, atol=1e-7)
+        np.testing.assert_allclose(res["out"][0], g["mixture"], rtol=0, atol=1e-6)
+
+
+def check_printed_gate():
+    g = _golden("printed_gate.json")
+    p = np.array([g["gate_probabilities"]])
+    z = np.log(p).astype(np.float32)
+    idx = O.select_topk(z, 2)
+    assert list(idx[0]) == g["top2_experts"]
+    probs = np.take_along_axis(O.softmax(z), idx, axis=1)[0]
+    np.testing.assert_allclose(probs, g["top2_probabilities"], rtol=1e-6)
+    w = O.topk_weights(z, idx)[0]
+    np.testing.assert_allclose(w, np.array([0.85, 0.08]) / 0.93, rtol=1e-6)
+
+
+def check_ln3_weights():
+    z = np.array([[0.0, math.log(3.0), -1.0]])
+    idx = O.select_topk(z, 2)
+    assert list(idx[0]) == [1, 0]
+    np.testing.assert_allclose(O.topk_weights(z, idx)[0], [0.75, 0.25], rtol=0, atol=1e-15)
+
+
+def check_weight_formulations():
+    """Renormalised top-k probabilities == softmax of the selected logits ([rkmt] §3.3
+    TinyMoE) == softmax with the unselected logits masked to -inf ([mlqm] §3.3)."""
+    rng = _rng(7)
+    for E, k in [(4, 2), (16, 2), (64, 2), (64, 6), (8, 8), (5, 1)]:
+        z = (rng.standard_normal((50, E)) * 3).astype(np.float32)
+        idx = O.select_topk(z, k)
+        w = O.topk_weights(z, idx)
+        zs = np.take_along_axis(z.astype(np.float64), idx, axis=1)
+        w2 = torch.softmax(torch.as_tensor(zs), dim=1).numpy()
+        masked = np.full(z.shape, -np.inf)
+        np.put_along_axis(masked, idx, zs, axis=1)
+        w3 = np.take_along_axis(torch.softmax(torch.as_tensor(masked), dim=1).numpy(), idx, axis=1)
+        np.testing.assert_allclose(w, w2, rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(w, w3, rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=1e-13)
+        assert np.all(w > 0) and np.all(w <= 1)
+        assert np.all(np.diff(w, axis=1) <= 1e-15)          # best slot first
+
+
+def _topk_brute(zrow, k):
+    """Enumerate all k-subsets; keep the largest sum of logits, ties to the
+    lexicographically smallest index tuple; return it best-first."""
+    best = min(itertools.combinations(range(len(zrow)), k),
+               key=lambda s: (-sum(float(zrow[e]) for e in s), s))
+    return sorted(best, key=lambda e: (-float(zrow[e]), e))
+
+
+def check_topk_bruteforce():
+    rng = _rng(11)
+    for E in range(1, 8):
+        for k in range(1, min(E, 3) + 1):
+            for _ in range(40):
+                z = rng.integers(-2, 3, size=(1, E)).astype(np.float32)  # many exact ties
+                assert list(O.select_topk(z, k)[0]) == _topk_brute(z[0], k)
+    assert sum(1 for _ in itertools.combinations(range(64), 2)) == \
+        _golden("ledgers.json")["pairs_of_64"]["combinations"]
+
+
+def check_topk_margin():
+    z = np.array([[1.0, 4.0, 2.5, 2.0]], np.float32)
+    np.testing.assert_allclose(O.topk_margin(z, 2), [0.5])
+    np.testing.assert_allclose(O.topk_margin(z, 1), [1.5])
+    assert np.isinf(O.topk_margin(z, 4)[0])
+
+
+def check_router_logits():
+    """One-hot tokens read out a row of W_r plus the bias; general inputs match a
+    float64 linear layer rounded to fp32."""
+    rng = _rng(3)
+    d, E = 16, 5
+    w_r = rng.standard_normal((d, E)).astype(np.float32)
+    b = rng.standard_normal(E).astype(np.float32)
+    x = np.eye(d, dtype=np.float32)[[3, 0, 15]]
+    z = O.router_logits(x, w_r, b)
+    np.testing.assert_array_equal(z, (w_r[[3, 0, 15]].astype(np.float64) + b).astype(np.float32))
+    x = rng.standard_normal((9, d))
+    ref = Fnn.linear(torch.as_tensor(x), torch.as_tensor(w_r.astype(np.float64)).T,
+                     torch.as_tensor(b.astype(np.float64))).numpy().astype(np.float32)
+    np.testing.assert_array_equal(O.router_logits(x, w_r, b), ref)
+    assert O.router_logits(x, w_r).shape == (9, E)
+
+
+def check_capacity_rule():
+    c = _golden("ledgers.json")["capacity"]
+    assert O.capacity_rule(c["T"], c["k"], c["E"]) == c["capacity"]
+    assert O.capacity_rule(10, 2, 4) == 5
+    assert O.capacity_rule(10, 1, 4) == 3          # ceil(2.5)
+    assert O.capacity_rule(1000, 2, 16, 1.25) == 157   # ceil(156.25)
+
+
+def _keep_bruteforce(idx, capacity):
+    """Slot (t, j) of expert e survives iff fewer than C earlier tokens chose e."""
+    T, k = idx.shape
+    keep = np.ones((T, k), bool)
+    for t in range(T):
+        for j in range(k):
+            earlier = sum(1 for t2 in range(t) if idx[t, j] in idx[t2])
+            keep[t, j] = capacity <= 0 or earlier < capacity
+    return keep
+
+
+def _random_idx(rng, T, E, k, skew=0.0):
+    z = rng.standard_normal((T, E)) + skew * np.arange(E)[None, ::-1]
+    return O.select_topk(z.astype(np.float32), k)
+
+
+def check_dispatch():
+    c = _golden("ledgers.json")["calls"]
+    T, E, k = c["T"], c["E"], c["k"]
+    idx = np.array([[(2 * t) % E, (2 * t + 1) % E] for t in range(T)])   # balanced
+    dp = O.dispatch(idx, E)
+    assert dp["counts"].sum() == c["calls"]
+    assert list(dp["counts"]) == [c["per_expert_balanced"]] * E
+    rng = _rng(5)
+    for (T, E, k, C, skew) in [(37, 5, 2, 0, 0), (64, 8, 3, 0, 1.0), (40, 4, 2, 6, 0.5),
+                               (25, 6, 1, 3, 2.0), (30, 3, 3, 100, 0), (20, 4, 2, 1, 0)]:
+        idx = _random_idx(rng, T, E, k, skew)
+        dp = O.dispatch(idx, E, C)
+        assert dp["counts"].sum() == T * k
+        np.testing.assert_array_equal(dp["counts"], np.bincount(idx.ravel(), minlength=E))
+        keep = _keep_bruteforce(idx, C)
+        np.testing.assert_array_equal(dp["inv"] >= 0, keep)
+        cap = C if C > 0 else T * k
+        np.testing.assert_array_equal(dp["kept"], np.minimum(dp["counts"], cap))
+        assert dp["n_dropped"] == int(np.maximum(dp["counts"] - cap, 0).sum())
+        # permutation = stable argsort of the expert of each kept slot
+        flat_e = idx.ravel()
+        kept_slots = np.nonzero(keep.ravel())[0]
+        order = kept_slots[np.argsort(flat_e[kept_slots], kind="stable")]
+        np.testing.assert_array_equal(dp["perm"], order)
+        np.testing.assert_array_equal(dp["offsets"], np.concatenate([[0], np.cumsum(dp["kept"])]))
+        inv = dp["inv"].ravel()
+        assert np.all(inv[dp["perm"]] == np.arange(len(dp["perm"])))    # bijection
+        if C >= T:
+            np.testing.assert_array_equal(dp["perm"], O.dispatch(idx, E, 0)["perm"])
+
+
+def check_activations():
+    assert O.gelu(np.array(0.0)) == 0.0 and O.silu(np.array(0.0)) == 0.0
+    np.testing.assert_allclose(O.gelu(np.array([1.0, -1.0])),
+                               [0.8413447460685429, -0.15865525393145707], rtol=1e-15)
+    np.testing.assert_allclose(O.silu(np.array([1.0, -2.0])),
+                               [1 / (1 + math.exp(-1)), -2 / (1 + math.exp(2))], rtol=1e-15)
+    v = np.linspace(-8, 8, 101)
+    np.testing.assert_allclose(O.gelu(v), Fnn.gelu(torch.as_tensor(v)).numpy(), rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(O.silu(v), Fnn.silu(torch.as_tensor(v)).numpy(), rtol=1e-13, atol=1e-15)
+
+
+def check_expert_ffn():
+    rng = _rng(9)
+    for act in ("gelu", "swiglu"):
+        wg, wu, wd = _rand_experts(rng, 1, 24, 40, act)
+        x = rng.standard_normal((7, 24))
+        got = O.expert_ffn(x, act, wg[0], None if wu is None else wu[0], wd[0])
+        ref = _torch_ffn(x, act, wg[0], None if wu is None else wu[0], wd[0])
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14)
+
+
+def check_layer_special_cases():
+    rng = _rng(21)
+    T, d, F = 33, 16, 24
+    for act in ("gelu", "swiglu"):
+        # E=1, k=1: a dense FFN
+        wg, wu, wd = _rand_experts(rng, 1, d, F, act)
+        x = rng.standard_normal((T, d))
+        w_r = rng.standard_normal((d, 1))
+        res = O.moe_layer(x, w_r, 1, act, wg, wu, wd)
+        np.testing.assert_allclose(res["out"], _torch_ffn(x, act, wg[0], None if wu is None else wu[0], wd[0]),
+                                   rtol=1e-12, atol=1e-13)
+        # identical experts: any routing gives FFN(x); a shared expert adds its own FFN
+        E, k = 6, 2
+        wg1, wu1, wd1 = _rand_experts(rng, 1, d, F, act)
+        rep = lambda a: None if a is None else np.repeat(a, E, axis=0)  # noqa: E731
+        w_r = rng.standard_normal((d, E))
+        bias = rng.standard_normal(E)
+        ffn = _torch_ffn(x, act, wg1[0], None if wu1 is None else wu1[0], wd1[0])
+        res = O.moe_layer(x, w_r, k, act, rep(wg1), rep(wu1), rep(wd1), bias=bias)
+        np.testing.assert_allclose(res["out"], ffn, rtol=1e-11, atol=1e-12)
+        sg, su, sd = _rand_experts(rng, 1, d, F, act)
+        shared = (sg[0], None if su is None else su[0], sd[0])
+        res = O.moe_layer(x, w_r, k, act, rep(wg1), rep(wu1), rep(wd1), bias=bias, shared=shared)
+        np.testing.assert_allclose(res["out"], ffn + _torch_ffn(x, act, *shared), rtol=1e-11, atol=1e-12)
+        # k = E without capacity: the dense soft mixture over all experts
+        E = 4
+        wg, wu, wd = _rand_experts(rng, E, d, F, act)
+        w_r = rng.standard_normal((d, E))
+        res = O.moe_layer(x, w_r, E, act, wg, wu, wd)
+        p = torch.softmax(torch.as_tensor(res["logits"].astype(np.float64)), dim=1).numpy()
+        dense = sum(p[:, e:e + 1] * _torch_ffn(x, act, wg[e], None if wu is None else wu[e], wd[e])
+                    for e in range(E))
+        np.testing.assert_allclose(res["out"], dense, rtol=1e-11, atol=1e-12)
+        # token permutation equivariance (no capacity)
+        res = O.moe_layer(x, w_r, 2, act, wg, wu, wd)
+        pi = rng.permutation(T)
+        res_p = O.moe_layer(x[pi], w_r, 2, act, wg, wu, wd)
+        np.testing.assert_allclose(res_p["out"], res["out"][pi], rtol=1e-12, atol=1e-14)
+        # a token whose every slot is dropped outputs zero (no shared expert)
+        res = O.moe_layer(x, w_r, 2, act, wg, wu, wd, capacity=1)
+        dead = np.all(res["inv"] < 0, axis=1)
+        assert dead.any()
+        assert np.all(res["out"][dead] == 0.0)
+        # a partly dropped token keeps its other weighted term, not renormalised
+        part = (res["inv"] >= 0).sum(axis=1) == 1
+        for t in np.nonzero(part)[0][:3]:
+            j = int(np.nonzero(res["inv"][t] >= 0)[0][0])
+            e = int(res["idx"][t, j])
+            y = _torch_ffn(x[t:t + 1], act, wg[e], None if wu is None else wu[e], wd[e])[0]
+            np.testing.assert_allclose(res["out"][t], res["w"][t, j] * y, rtol=1e-12, atol=1e-14)
+
+
+def check_ledgers():
+    a = _golden("ledgers.json")["active_params"]
+    assert O.active_params(0, a["routed_total"], a["E"], a["k"]) == a["routed_active"]
+    assert O.active_params(a["common"], a["routed_total"], a["E"], a["k"]) == a["active"]
+    assert abs(a["active"] / a["total"] - 0.3) < 1e-12
+    assert O.expert_weight_bytes(64, 4096, 14336, "swiglu", 2) == 64 * 3 * 4096 * 14336 * 2
+    assert abs(O.expert_weight_bytes(64, 4096, 14336, "swiglu", 2) / 1e9 - 22.55) < 0.01
+    assert O.expert_weight_bytes(4, 64, 128, "gelu", 4) == 4 * 2 * 64 * 128 * 4
+
+
+PINS = [check_worked_combine, check_worked_layer, check_printed_gate, check_ln3_weights,
+        check_weight_formulations, check_topk_bruteforce, check_topk_margin,
+        check_router_logits, check_capacity_rule, check_dispatch, check_activations,
+        check_expert_ffn, check_layer_special_cases, check_ledgers]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(pin):
+    pin()
+
+
+# ---------------------------------------------------------------------------------
+# Planted mistakes: each must be caught by at least one pin
+# ---------------------------------------------------------------------------------
+def _fails(monkeypatch, name, bad):
+    monkeypatch.setattr(O, name, bad)
+    caught = []
+    for pin in PINS:
+        try:
+            pin()
+        except Exception:  # noqa: BLE001 - any failure of a pin counts as caught
+            caught.append(pin.__name__)
+    return caught
+
+
+_orig = {n: getattr(O, n) for n in ("expert_order", "topk_weights", "dispatch", "expert_ffn",
+                                    "combine", "router_logits", "gelu", "silu", "capacity_rule",
+                                    "active_params")}
+
+
+def _mut_highest_index_ties(z):
+    E = np.asarray(z).shape[1]
+    return (E - 1 - np.argsort(-np.asarray(z, np.float64)[:, ::-1], axis=1, kind="stable"))
+
+
+def _mut_inverted_weights(z, idx):
+    zs = np.take_along_axis(np.asarray(z, np.float64), idx, axis=1)
+    e = np.exp(zs[:, :1] - zs)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def _mut_keep_latest(idx, E, capacity=0):
+    res = _orig["dispatch"](idx, E, 0)
+    if capacity <= 0:
+        return res
+    keep = (_orig["dispatch"](idx[::-1], E, capacity)["inv"] >= 0)[::-1]
+    return dict(res, inv=np.where(keep, res["inv"], -1),
+                kept=np.minimum(res["counts"], capacity), n_dropped=int((~keep).sum()))
+
+
+def _mut_transposed_down(xr, act, wg, wu, wd):
+    return _orig["expert_ffn"](xr, act, wg, wu, np.ascontiguousarray(wd.T).reshape(wd.shape))
+
+
+def _mut_unweighted(y, w, keep=None, shared=None):
+    return _orig["combine"](y, np.ones_like(np.asarray(w, np.float64)), keep, shared)
+
+
+def _mut_no_shared(y, w, keep=None, shared=None):
+    return _orig["combine"](y, w, keep, None)
+
+
+def _mut_bias_dropped(x, w_r, bias=None):
+    return _orig["router_logits"](x, w_r, None)
+
+
+def _mut_tanh_gelu(v):
+    v = np.asarray(v, np.float64)
+    return 0.5 * v * (1 + np.tanh(math.sqrt(2 / math.pi) * (v + 0.044715 * v ** 3)))
+
+
+def _mut_sigmoid_only(v):
+    return 1.0 / (1.0 + np.exp(-np.asarray(v, np.float64)))
+
+
+def _mut_capacity_floor_no_k(T, k, E, factor=1.0):
+    return int(factor * T / E)
+
+
+def _mut_ledger_no_k(common, routed_total, E, k):
+    return common + routed_total / E
+
+
+MUTATIONS = [("expert_order", _mut_highest_index_ties), ("topk_weights", _mut_inverted_weights),
+             ("dispatch", _mut_keep_latest), ("expert_ffn", _mut_transposed_down),
+             ("combine", _mut_unweighted), ("combine", _mut_no_shared),
+             ("router_logits", _mut_bias_dropped), ("gelu", _mut_tanh_gelu),
+             ("silu", _mut_sigmoid_only), ("capacity_rule", _mut_capacity_floor_no_k),
+             ("active_params", _mut_ledger_no_k)]
+
+
+@pytest.mark.parametrize("name,bad", MUTATIONS, ids=[m[1].__name__ for m in MUTATIONS])
+def test_mutation_is_caught(monkeypatch, name, bad):
+    caught = _fails(monkeypatch, name, bad)
+    assert caught, f"planted mistake in {name} ({bad.__name__}) passed every pin"
