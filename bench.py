@@ -1,0 +1,206 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE-layer forward on one MI355X.
+
+Workload (default): the prefill-shaped layer with E=64 experts, top-2, T=4096 tokens,
+d=4096, SwiGLU experts of width 14336, bf16 weights/activations, fp32 router logits and
+accumulation; seeded synthetic inputs and random-init weights resident in HBM.
+A step is one moe_layer_forward (route, dispatch, grouped expert FFN, combine).
+
+Prints ONE JSON line: tokens/s, the roofline of the dominant kernel (the gate/up grouped
+GEMM) measured with HIP events recorded by the library on its stream, and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
+RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, help="workload number 1-5 (default 2: prefill, E=64)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-experts", type=int, default=8,
+                    help="experts whose rows the CPU oracle computes for its timed sample")
+    return ap.parse_args()
+
+
+def layer_counts(cfg, L):
+    offsets = L.offsets.cpu().numpy().astype(np.int64)
+    kept = np.diff(offsets)
+    touched = int((kept > 0).sum())
+    rows = int(kept.sum())
+    return kept, touched, rows
+
+
+def algorithmic(cfg, touched, rows):
+    """Bytes and flops the method must touch (weights of touched experts once, x once,
+    outputs once), per stage and for the whole layer."""
+    b = 2 if cfg.dtype == "bf16" else 4
+    mats_up = 2 if cfg.act == "swiglu" else 1
+    T, d, F, E = cfg.T, cfg.d, cfg.F, cfg.E
+    sh_rows = T if cfg.shared else 0
+    n_exp = touched + (1 if cfg.shared else 0)
+    up_bytes = n_exp * mats_up * F * d * b + T * d * b + (rows + sh_rows) * F * b
+    up_flops = 2.0 * (rows + sh_rows) * F * d * mats_up
+    down_bytes = n_exp * d * F * b + (rows + sh_rows) * F * b + (rows + sh_rows) * d * 4
+    down_flops = 2.0 * (rows + sh_rows) * d * F
+    layer_bytes = n_exp * (mats_up + 1) * F * d * b + T * d * b + d * E * b + T * d * b
+    layer_flops = 2.0 * T * d * E + up_flops + down_flops
+    return dict(up_bytes=up_bytes, up_flops=up_flops, down_bytes=down_bytes, down_flops=down_flops,
+                layer_bytes=layer_bytes, layer_flops=layer_flops)
+
+
+def roofline(bytes_, flops, seconds, dtype):
+    ai = flops / bytes_
+    peak_t = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_F32_TFLOPS
+    ridge = peak_t * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if ai < ridge:
+        a = bytes_ / seconds / 1e9
+        return dict(bound="hbm", achieved=round(a, 1), peak=PEAK_HBM_GBS, unit="GB/s", frac=round(a / PEAK_HBM_GBS, 4))
+    a = flops / seconds / 1e12
+    return dict(bound="mfma" if dtype == "bf16" else "alu", achieved=round(a, 1), peak=peak_t, unit="TFLOP/s",
+                frac=round(a / peak_t, 4))
+
+
+def cpu_baseline(cfg, inp, L, n_exp):
+    """The oracle, as it stands, on a bounded sample: routing and dispatch of all T tokens,
+    then the FFN of every row routed to the first n_exp touched experts and their
+    weighted contribution.  Tokens-equivalent = rows / k."""
+    from oracle import moe_oracle as O
+    from sparse_mixture_experts_27_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    x64 = synth.to_numpy(inp["x"])
+    wr64 = synth.to_numpy(inp["w_r"])
+    b64 = synth.to_numpy(inp["bias"])
+    t0 = time.perf_counter()
+    z = O.router_logits(x64, wr64, b64)
+    idx = O.select_topk(z, cfg.k)
+    w = O.topk_weights(z, idx)
+    dp = O.dispatch(idx, cfg.E, cfg.capacity)
+    t_route = time.perf_counter() - t0
+    kept = np.diff(dp["offsets"])
+    experts = [int(e) for e in np.nonzero(kept)[0][:n_exp]]
+    t_ffn, rows = 0.0, 0
+    for e in experts:
+        wts = (synth.to_numpy(inp["w_gate"][e]),
+               None if inp["w_up"] is None else synth.to_numpy(inp["w_up"][e]),
+               synth.to_numpy(inp["w_down"][e]))
+        r = np.arange(dp["offsets"][e], dp["offsets"][e + 1])
+        slots = dp["perm"][r]
+        tok, j = slots // cfg.k, slots % cfg.k
+        t1 = time.perf_counter()
+        y = O.expert_ffn(x64[tok], cfg.act, *wts)
+        contrib = w[tok, j][:, None] * y          # this expert's share of the combine
+        t_ffn += time.perf_counter() - t1
+        rows += len(r)
+        del wts, y, contrib
+    total = t_route + t_ffn
+    tokens_equiv = rows / cfg.k
+    return dict(value=round(tokens_equiv / total, 2), unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=(f"{cfg.name}: routing+dispatch of all {cfg.T} tokens, FFN+combine of the {rows} rows "
+                        f"routed to {len(experts)} experts (= {tokens_equiv:.0f} token-equivalents), "
+                        f"float64 numpy, {total:.1f} s"),
+                seconds=round(total, 2))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer runs on a single MI355X; see DESIGN.md for how it would shard).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from sparse_mixture_experts_27_amd import binding as B
+    from sparse_mixture_experts_27_amd import synth
+    from sparse_mixture_experts_27_amd.configs import CONFIGS
+
+    cfg = CONFIGS[args.config]
+    B.lib()                                  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    inp = synth.make_inputs(cfg, dev)
+    L = B.Layer(inp["w_r"], inp["w_gate"], inp["w_up"], inp["w_down"], cfg.k, act=cfg.act, bias=inp["bias"],
+                capacity=cfg.capacity, s_gate=inp["s_gate"], s_up=inp["s_up"], s_down=inp["s_down"])
+    x = inp["x"]
+    for _ in range(args.warmup):
+        L(x)
+    torch.cuda.synchronize()
+
+    evs = []
+    for _ in range(args.steps):
+        row = [torch.cuda.Event(enable_timing=True) for _ in range(B.STAGE_EVENTS)]
+        for e in row:
+            e.record()                           # create the underlying HIP events
+        evs.append(row)
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        L(x, stage_events=evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    stage_ms = {name: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
+                for j, name in enumerate(B.STAGES)}
+    ms_step = elapsed / args.steps * 1e3
+    value = cfg.T * args.steps / elapsed
+    kept, touched, rows = layer_counts(cfg, L)
+    alg = algorithmic(cfg, touched, rows)
+    up_s = stage_ms["ffn_up"] / 1e3
+    roof = roofline(alg["up_bytes"], alg["up_flops"], up_s, cfg.dtype)
+    roof["traffic"] = None
+    roof["kernel"] = "ffn_gemm_bf16_kernel<SwiGLU up>" if cfg.dtype == "bf16" else "ffn_gemm_f32_kernel<up>"
+    layer_roof = roofline(alg["layer_bytes"], alg["layer_flops"], ms_step / 1e3, cfg.dtype)
+    down_roof = roofline(alg["down_bytes"], alg["down_flops"], stage_ms["ffn_down"] / 1e3, cfg.dtype)
+
+    line = {
+        "metric": "MoE-layer tokens/s at E=64,k=2; % bf16 MFMA peak (prefill), % HBM BW (decode)",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) hidden states, N(0,1/fan_in) random-init weights)",
+        "config": {"workload": cfg.label, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k, "F": cfg.F,
+                   "act": cfg.act, "shared": cfg.shared, "capacity": cfg.capacity, "parallelism": "single-gpu"},
+        "roofline": roof,
+        "layer_roofline": layer_roof,
+        "down_roofline": down_roof,
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "routing": {"touched_experts": touched, "rows": rows, "load_min": int(kept.min()),
+                    "load_max": int(kept.max()), "n_dropped": int(L.n_dropped.item())},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, inp, L, args.cpu_experts)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

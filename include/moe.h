@@ -1,0 +1,204 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) sparse Mixture-of-Experts layer forward.
+ *
+ * The library computes the forward pass of one sparse MoE layer:
+ *   router linear -> softmax / top-k -> optional per-expert capacity with token
+ *   dropping -> dispatch into an expert-sorted permutation -> per-expert FFN
+ *   (grouped GEMM) -> routing-weighted combine (+ optional shared expert).
+ *
+ * Sources, cited by page and section:
+ *   [mlqm]   www.mlqm.cn/news/130088: §3.1 Router (logits = h W_r, softmax, top-k),
+ *            §3.3 Gate (w_i = p_i / (p_i + p_j), -inf masking), §4.2 model code.
+ *   [rkmt]   "大模型MoE架构揭秘：为什么总参数≠激活参数": §2.3 expert capacity (T*k)/E,
+ *            overflow tokens dropped.
+ *   [200B-5] "[从零训练一个200B大语言模型] 5/25：MoE怎样用一部分参数，完成一次计算？":
+ *            "谁来决定请哪几个专家？" (router, top-k, weighted mixture of the selected
+ *            experts' outputs), "共享专家，给每个token都走的一条路" (shared expert).
+ *   [cnnet]  "MoE混合专家架构原理与工程实践：解密大模型稀疏计算真相": stacked ("fused")
+ *            expert weights sliced by index, batching the tokens of one expert.
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless stated otherwise.  The caller allocates and
+ *     owns every input, output and workspace buffer; the library never allocates,
+ *     frees, copies to or from the host, or synchronises.
+ *   - Every call validates its arguments on the host first.  On any error it returns
+ *     a non-zero status before launching anything, so no output is touched.
+ *     moe_last_error() then describes the problem (thread-local string).
+ *   - On MOE_OK all work has been enqueued on `stream` (in stream order); results are
+ *     visible after the caller synchronises the stream.  A kernel launch failure
+ *     returns MOE_EHIP (work enqueued before it may have run).
+ *   - Matrices are row-major and contiguous.  Expert weights use the nn.Linear
+ *     layout [out, in]: w_gate / w_up are [G, F, d] and w_down is [G, d, F].
+ *   - dtype MOE_BF16: x, w_r and expert weights are bfloat16; products are exact in
+ *     fp32 and accumulate in fp32; the hidden activation of the expert is rounded to
+ *     bf16 once.  MOE_F32: everything is fp32.  Logits, routing weights and the
+ *     per-row expert outputs y are always fp32.
+ *   - Requirements: T >= 0 (T == 0 is a no-op), d >= 1, 1 <= E <= 1024,
+ *     1 <= k <= E, F >= 1; for MOE_BF16 expert FFNs, d and F must be multiples of 64
+ *     (MOE_EUNSUPPORTED otherwise).  Pointers must be 16-byte aligned.
+ *   - Calls on the same stream are ordered; concurrent calls on different streams
+ *     share no library state.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,        /* null required pointer, bad size or enum */
+  MOE_EUNSUPPORTED = 2,  /* valid but unsupported shape (e.g. bf16 d % 64 != 0) */
+  MOE_EWORKSPACE = 3,    /* workspace smaller than the *_workspace_bytes() figure */
+  MOE_EHIP = 4           /* a HIP launch or runtime call failed */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+typedef enum { MOE_ACT_GELU = 0, MOE_ACT_SWIGLU = 1 } moe_act_t;
+
+/* Static description of a status code (host). */
+const char* moe_status_string(moe_status_t s);
+/* Message of the last failing call on this host thread ("" if none). */
+const char* moe_last_error(void);
+
+/*
+ * moe_route - router logits, top-k selection and routing weights.
+ *   [mlqm] §3.1: logits z = h W_r (+ per-expert offset b), softmax over E experts,
+ *   keep the k best.  [mlqm] §3.3 / §4.2: the kept probabilities are renormalised,
+ *   w_j = p_{s_j} / sum_i p_{s_i} = exp(z_{s_j} - z_{s_0}) / sum_i exp(z_{s_i} - z_{s_0}).
+ *   x        [T, d]   dtype dt
+ *   w_r      [d, E]   dtype dt
+ *   bias     [E] fp32 or NULL (no offsets)
+ *   topk_idx [T, k] int32 out: expert of slot j, slots ordered by descending logit;
+ *            equal logits are ordered by ascending expert index
+ *   topk_w   [T, k] fp32 out: routing weights (sum to 1 per token)
+ *   logits   [T, E] fp32 out: the router logits (fp32 accumulation)
+ * Deterministic: identical inputs give identical bits.
+ */
+moe_status_t moe_route(const void* x, const void* w_r, const float* bias, moe_dtype_t dt,
+                       int64_t T, int64_t d, int32_t E, int32_t k,
+                       int32_t* topk_idx, float* topk_w, float* logits, hipStream_t stream);
+
+/* Workspace bytes moe_dispatch needs for T tokens and E experts (host, pure). */
+size_t moe_dispatch_workspace_bytes(int64_t T, int32_t E);
+
+/*
+ * moe_dispatch - per-expert counts, capacity, expert-sorted permutation.
+ *   [rkmt] §2.3: expert e accepts at most `capacity` slots; the rest are dropped
+ *   (zero contribution).  The earliest tokens (ascending token index) are kept.
+ *   topk_idx  [T, k] int32 in  (values in [0, E); other values are undefined behaviour)
+ *   capacity  <= 0: unlimited
+ *   counts    [E] int32 out: slots that selected e (demand, before capacity)
+ *   offsets   [E+1] int32 out: exclusive prefix sum of kept = min(counts, capacity)
+ *   perm      [T*k] int32 out: perm[r] = t*k + j for each kept row r < offsets[E];
+ *             rows of one expert are in ascending token order; entries >= offsets[E]
+ *             are left untouched
+ *   inv       [T*k] int32 out: row of slot (t, j), or -1 when the slot was dropped
+ *   n_dropped [1] int32 out: number of dropped slots
+ *   ws        device workspace of at least moe_dispatch_workspace_bytes(T, E) bytes
+ * Integer-only and deterministic (bit-identical across runs).
+ */
+moe_status_t moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t E, int32_t k,
+                          int64_t capacity, int32_t* counts, int32_t* offsets, int32_t* perm,
+                          int32_t* inv, int32_t* n_dropped, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* Workspace bytes moe_expert_ffn needs (host, pure). */
+size_t moe_expert_ffn_workspace_bytes(int64_t max_rows, int32_t G, int64_t d, int64_t F,
+                                      moe_act_t act, moe_dtype_t dt);
+
+/*
+ * moe_expert_ffn - every group's FFN over its rows (grouped GEMM).
+ *   [cnnet]: experts stacked in one tensor and sliced by index; the rows routed to one
+ *   expert are computed together.  GeLU expert: y = W2 gelu(W1 x) with w_gate = W1
+ *   [G,F,d], w_down = W2 [G,d,F], w_up = NULL.  SwiGLU expert:
+ *   y = Wd (silu(Wg x) * (Wu x)) with w_gate = Wg, w_up = Wu [G,F,d], w_down = Wd.
+ *   x        [n_x, d] dtype dt
+ *   perm     NULL: row r reads x[r];  else row r reads x[perm[r] / k]
+ *   offsets  [G+1] int32 (device): group g owns rows [offsets[g], offsets[g+1]),
+ *            non-decreasing, offsets[0] >= 0.  Rows at or beyond max_rows are ignored.
+ *   max_rows host upper bound of offsets[G] (sizes the launch and the workspace)
+ *   y        [max_rows, d] fp32 out: y[r] for r < min(offsets[G], max_rows)
+ *   ws       device workspace of moe_expert_ffn_workspace_bytes(...) bytes
+ */
+moe_status_t moe_expert_ffn(const void* x, const int32_t* perm, int32_t k,
+                            const int32_t* offsets, int32_t G, int64_t max_rows,
+                            int64_t d, int64_t F, moe_act_t act, moe_dtype_t dt,
+                            const void* w_gate, const void* w_up, const void* w_down,
+                            float* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_combine - routing-weighted sum of the selected experts' outputs.
+ *   [200B-5] "谁来决定请哪几个专家？": out = sum_j w_j * Expert_j(x) (the worked example
+ *   0.75*[0.8,0.2,-0.4] + 0.25*[0.4,0.6,0.8] = [0.7,0.3,-0.1]); "共享专家…": the
+ *   shared expert's result is added.  A dropped slot (inv < 0) adds nothing and the
+ *   other weights are not renormalised.  Accumulates in fp32, rounds once to out_dt.
+ *   y       [y_rows, d] fp32 expert outputs in row order
+ *   inv     [T, k] int32 row of each slot, -1 = dropped (rows >= y_rows are ignored)
+ *   topk_w  [T, k] fp32 routing weights
+ *   shared  [T, d] fp32 shared-expert output, or NULL
+ *   out     [T, d] out, dtype out_dt
+ */
+moe_status_t moe_combine(const float* y, int64_t y_rows, const int32_t* inv,
+                         const float* topk_w, const float* shared, int64_t T, int64_t d,
+                         int32_t k, moe_dtype_t out_dt, void* out, hipStream_t stream);
+
+/* Arguments of the whole layer (host struct; pointers inside are device pointers). */
+typedef struct moe_layer_args {
+  int32_t dt;            /* moe_dtype_t: activations and weights */
+  int32_t act;           /* moe_act_t */
+  int32_t out_dt;        /* moe_dtype_t of `out`: MOE_F32 (0, the fp32 accumulator rounded
+                            once) or MOE_BF16 (rounded once to bf16) */
+  int64_t T, d, F;
+  int32_t E, k;
+  int64_t capacity;      /* <= 0: unlimited */
+  const void* x;         /* [T, d] */
+  const void* w_r;       /* [d, E] */
+  const float* bias;     /* [E] router offsets or NULL */
+  const void* w_gate;    /* [E, F, d] */
+  const void* w_up;      /* [E, F, d], NULL for GeLU */
+  const void* w_down;    /* [E, d, F] */
+  const void* s_gate;    /* shared expert [F, d], or NULL for none */
+  const void* s_up;      /* [F, d] (SwiGLU) or NULL */
+  const void* s_down;    /* [d, F] */
+  void* out;             /* [T, d] out, dtype out_dt */
+  /* Optional outputs; NULL keeps them inside the workspace. */
+  int32_t* topk_idx;     /* [T, k] */
+  float* topk_w;         /* [T, k] */
+  float* logits;         /* [T, E] */
+  int32_t* counts;       /* [E] */
+  int32_t* offsets;      /* [E+1] */
+  int32_t* perm;         /* [T*k] */
+  int32_t* inv;          /* [T*k] */
+  int32_t* n_dropped;    /* [1] */
+  void* ws;              /* device workspace */
+  size_t ws_bytes;
+  /* Optional measurement hook: NULL, or MOE_STAGE_EVENTS hipEvent_t handles created by
+     the caller.  Event i is recorded on `stream` right after stage boundary i:
+     0 start, 1 route, 2 dispatch, 3 FFN schedule, 4 FFN up-projection (gate/up GEMM),
+     5 FFN down-projection, 6 combine.  The library only records them. */
+  void* const* stage_events;
+} moe_layer_args_t;
+
+#define MOE_STAGE_EVENTS 7
+
+/* Workspace bytes moe_layer_forward needs for these arguments (host, pure). */
+size_t moe_layer_workspace_bytes(const moe_layer_args_t* a);
+
+/*
+ * moe_layer_forward - the whole layer on one stream:
+ *   route -> dispatch -> grouped expert FFN (the shared expert runs as one more group
+ *   over all T tokens) -> combine.  No host synchronisation inside.
+ *   Result: out[t] = shared(x_t) + sum_{kept j} w_{t,j} * Expert_{idx_{t,j}}(x_t).
+ */
+moe_status_t moe_layer_forward(const moe_layer_args_t* a, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,275 @@
+"""Thin ctypes binding of libmoe.so (the C ABI in include/moe.h).
+
+Argument marshalling only: every step of the layer runs in the HIP library.  Torch
+tensors provide device memory and the current HIP stream.  If the library is missing
+the calls raise; there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+_lib = None
+
+MOE_F32, MOE_BF16 = 0, 1
+MOE_ACT_GELU, MOE_ACT_SWIGLU = 0, 1
+STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EUNSUPPORTED", 3: "MOE_EWORKSPACE", 4: "MOE_EHIP"}
+
+# entry points declared in include/moe.h
+EXPORTS = ("moe_status_string", "moe_last_error", "moe_route", "moe_dispatch_workspace_bytes",
+           "moe_dispatch", "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine",
+           "moe_layer_workspace_bytes", "moe_layer_forward")
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class LayerArgs(C.Structure):
+    _fields_ = [("dt", C.c_int32), ("act", C.c_int32), ("out_dt", C.c_int32),
+                ("T", C.c_int64), ("d", C.c_int64), ("F", C.c_int64),
+                ("E", C.c_int32), ("k", C.c_int32), ("capacity", C.c_int64),
+                ("x", C.c_void_p), ("w_r", C.c_void_p), ("bias", C.c_void_p),
+                ("w_gate", C.c_void_p), ("w_up", C.c_void_p), ("w_down", C.c_void_p),
+                ("s_gate", C.c_void_p), ("s_up", C.c_void_p), ("s_down", C.c_void_p),
+                ("out", C.c_void_p),
+                ("topk_idx", C.c_void_p), ("topk_w", C.c_void_p), ("logits", C.c_void_p),
+                ("counts", C.c_void_p), ("offsets", C.c_void_p), ("perm", C.c_void_p),
+                ("inv", C.c_void_p), ("n_dropped", C.c_void_p),
+                ("ws", C.c_void_p), ("ws_bytes", C.c_size_t),
+                ("stage_events", C.POINTER(C.c_void_p))]
+
+STAGE_EVENTS = 7
+STAGES = ("route", "dispatch", "ffn_schedule", "ffn_up", "ffn_down", "combine")
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load libmoe.so once; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                               "`python -m sparse_mixture_experts_27_amd.build`")
+        L = C.CDLL(_LIB_PATH)
+        vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+        L.moe_status_string.restype = C.c_char_p
+        L.moe_status_string.argtypes = [C.c_int]
+        L.moe_last_error.restype = C.c_char_p
+        L.moe_last_error.argtypes = []
+        L.moe_route.restype = C.c_int
+        L.moe_route.argtypes = [vp, vp, vp, C.c_int, i64, i64, i32, i32, vp, vp, vp, vp]
+        L.moe_dispatch_workspace_bytes.restype = sz
+        L.moe_dispatch_workspace_bytes.argtypes = [i64, i32]
+        L.moe_dispatch.restype = C.c_int
+        L.moe_dispatch.argtypes = [vp, i64, i32, i32, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_expert_ffn_workspace_bytes.restype = sz
+        L.moe_expert_ffn_workspace_bytes.argtypes = [i64, i32, i64, i64, C.c_int, C.c_int]
+        L.moe_expert_ffn.restype = C.c_int
+        L.moe_expert_ffn.argtypes = [vp, vp, i32, vp, i32, i64, i64, i64, C.c_int, C.c_int,
+                                     vp, vp, vp, vp, vp, sz, vp]
+        L.moe_combine.restype = C.c_int
+        L.moe_combine.argtypes = [vp, i64, vp, vp, vp, i64, i64, i32, C.c_int, vp, vp]
+        L.moe_layer_workspace_bytes.restype = sz
+        L.moe_layer_workspace_bytes.argtypes = [C.POINTER(LayerArgs)]
+        L.moe_layer_forward.restype = C.c_int
+        L.moe_layer_forward.argtypes = [C.POINTER(LayerArgs), vp]
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise MoEError(status, lib().moe_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device=None):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _req(t: Optional[torch.Tensor], name: str, dtype=None, device=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------------------------
+def route(x, w_r, k, bias=None):
+    """-> (topk_idx int32 [T,k], topk_w f32 [T,k], logits f32 [T,E])."""
+    T, d = x.shape
+    E = w_r.shape[1]
+    for t, n in ((x, "x"), (w_r, "w_r")):
+        _req(t, n, x.dtype, x.device)
+    _req(bias, "bias", torch.float32, x.device)
+    idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    _check(lib().moe_route(_ptr(x), _ptr(w_r), _ptr(bias), _dt(x), T, d, E, k,
+                           _ptr(idx), _ptr(w), _ptr(logits), _stream(x.device)))
+    return idx, w, logits
+
+
+@dataclass
+class Dispatch:
+    counts: torch.Tensor
+    offsets: torch.Tensor
+    perm: torch.Tensor
+    inv: torch.Tensor
+    n_dropped: torch.Tensor
+
+
+def dispatch(topk_idx, E, capacity=0) -> Dispatch:
+    _req(topk_idx, "topk_idx", torch.int32)
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.full((T * k,), -1, dtype=torch.int32, device=dev)
+    inv = torch.empty((T, k), dtype=torch.int32, device=dev)
+    nd = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = _ws(lib().moe_dispatch_workspace_bytes(T, E), dev)
+    _check(lib().moe_dispatch(_ptr(topk_idx), T, E, k, int(capacity), _ptr(counts), _ptr(offsets),
+                              _ptr(perm), _ptr(inv), _ptr(nd), _ptr(ws), ws.numel(), _stream(dev)))
+    return Dispatch(counts, offsets, perm, inv, nd)
+
+
+def expert_ffn(x, offsets, w_gate, w_up, w_down, max_rows, perm=None, k=1, act="swiglu"):
+    """-> y f32 [max_rows, d] (rows past offsets[G] unspecified)."""
+    G = w_gate.shape[0]
+    F, d = w_gate.shape[1], w_gate.shape[2]
+    dev = x.device
+    for t, n in ((x, "x"), (w_gate, "w_gate"), (w_up, "w_up"), (w_down, "w_down")):
+        _req(t, n, x.dtype, dev)
+    _req(offsets, "offsets", torch.int32, dev)
+    _req(perm, "perm", torch.int32, dev)
+    a = MOE_ACT_SWIGLU if act == "swiglu" else MOE_ACT_GELU
+    y = torch.empty((max(max_rows, 1), d), dtype=torch.float32, device=dev)
+    ws = _ws(lib().moe_expert_ffn_workspace_bytes(max_rows, G, d, F, a, _dt(x)), dev)
+    _check(lib().moe_expert_ffn(_ptr(x), _ptr(perm), k, _ptr(offsets), G, max_rows, d, F, a, _dt(x),
+                                _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(y), _ptr(ws), ws.numel(),
+                                _stream(dev)))
+    return y[:max_rows]
+
+
+def combine(y, inv, topk_w, out_dtype, shared=None):
+    """-> out [T, d] of out_dtype."""
+    T, k = inv.shape
+    d = y.shape[1]
+    dev = inv.device
+    _req(y, "y", torch.float32, dev)
+    _req(inv, "inv", torch.int32, dev)
+    _req(topk_w, "topk_w", torch.float32, dev)
+    _req(shared, "shared", torch.float32, dev)
+    out = torch.empty((T, d), dtype=out_dtype, device=dev)
+    _check(lib().moe_combine(_ptr(y), y.shape[0], _ptr(inv), _ptr(topk_w), _ptr(shared), T, d, k,
+                             MOE_BF16 if out_dtype == torch.bfloat16 else MOE_F32, _ptr(out),
+                             _stream(dev)))
+    return out
+
+
+class Layer:
+    """One MoE layer with its weights; forward() runs moe_layer_forward.
+
+    Buffers for the output, the routing results and the workspace are allocated once
+    (per token count) and reused, so repeated calls allocate nothing.
+    """
+
+    def __init__(self, w_r, w_gate, w_up, w_down, k, act="swiglu", bias=None, capacity=0,
+                 s_gate=None, s_up=None, s_down=None, out_dtype=torch.float32):
+        self.w_r, self.bias = w_r, bias
+        self.w_gate, self.w_up, self.w_down = w_gate, w_up, w_down
+        self.s_gate, self.s_up, self.s_down = s_gate, s_up, s_down
+        self.k, self.capacity = k, int(capacity)
+        if out_dtype not in (torch.float32, torch.bfloat16):
+            raise TypeError("out_dtype must be float32 or bfloat16")
+        self.out_dtype = out_dtype
+        self.act = MOE_ACT_SWIGLU if act == "swiglu" else MOE_ACT_GELU
+        self.E = w_r.shape[1]
+        self.F, self.d = w_gate.shape[1], w_gate.shape[2]
+        dev = w_r.device
+        for t, n in ((w_r, "w_r"), (w_gate, "w_gate"), (w_up, "w_up"), (w_down, "w_down"),
+                     (s_gate, "s_gate"), (s_up, "s_up"), (s_down, "s_down")):
+            _req(t, n, w_r.dtype, dev)
+        _req(bias, "bias", torch.float32, dev)
+        self._T = None
+
+    def _args(self, x):
+        T = x.shape[0]
+        a = LayerArgs()
+        a.dt, a.act = _dt(x), self.act
+        a.out_dt = MOE_BF16 if self.out_dtype == torch.bfloat16 else MOE_F32
+        a.T, a.d, a.F, a.E, a.k, a.capacity = T, self.d, self.F, self.E, self.k, self.capacity
+        a.x, a.w_r, a.bias = _ptr(x), _ptr(self.w_r), _ptr(self.bias)
+        a.w_gate, a.w_up, a.w_down = _ptr(self.w_gate), _ptr(self.w_up), _ptr(self.w_down)
+        a.s_gate, a.s_up, a.s_down = _ptr(self.s_gate), _ptr(self.s_up), _ptr(self.s_down)
+        return a
+
+    def _buffers(self, x):
+        T, dev, k = x.shape[0], x.device, self.k
+        if self._T == T and self._dev == dev and self._dtype == x.dtype:
+            return
+        self.out = torch.empty((T, self.d), dtype=self.out_dtype, device=dev)
+        self.topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.logits = torch.empty((T, self.E), dtype=torch.float32, device=dev)
+        self.counts = torch.empty(self.E, dtype=torch.int32, device=dev)
+        self.offsets = torch.empty(self.E + 1, dtype=torch.int32, device=dev)
+        self.perm = torch.empty(T * k, dtype=torch.int32, device=dev)
+        self.inv = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.n_dropped = torch.empty(1, dtype=torch.int32, device=dev)
+        self.ws = _ws(lib().moe_layer_workspace_bytes(C.byref(self._args(x))), dev)
+        self._T, self._dev, self._dtype = T, dev, x.dtype
+
+    def forward(self, x, stage_events=None):
+        """stage_events: optional list of 7 torch.cuda.Event (already created) recorded at
+        the stage boundaries on the current stream."""
+        _req(x, "x", self.w_r.dtype, self.w_r.device)
+        self._buffers(x)
+        a = self._args(x)
+        a.out = _ptr(self.out)
+        a.topk_idx, a.topk_w, a.logits = _ptr(self.topk_idx), _ptr(self.topk_w), _ptr(self.logits)
+        a.counts, a.offsets, a.perm = _ptr(self.counts), _ptr(self.offsets), _ptr(self.perm)
+        a.inv, a.n_dropped = _ptr(self.inv), _ptr(self.n_dropped)
+        a.ws, a.ws_bytes = _ptr(self.ws), self.ws.numel()
+        if stage_events is not None:
+            if len(stage_events) != STAGE_EVENTS:
+                raise ValueError(f"need {STAGE_EVENTS} events")
+            arr = (C.c_void_p * STAGE_EVENTS)(*[ev.cuda_event for ev in stage_events])
+            a.stage_events = C.cast(arr, C.POINTER(C.c_void_p))
+        _check(lib().moe_layer_forward(C.byref(a), _stream(x.device)))
+        return self.out
+
+    __call__ = forward

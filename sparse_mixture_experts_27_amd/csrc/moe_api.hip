@@ -1,0 +1,275 @@
+// C-ABI entry points: host-side validation, workspace carving, launches.
+// The layer forward chains route -> dispatch -> grouped FFN -> combine on one stream
+// ([mlqm] §4.2 forward steps 1-4; [200B-5] "谁来决定请哪几个专家？" and "共享专家…").
+#include "moe_common.h"
+
+#include <mutex>
+#include <set>
+#include <utility>
+
+namespace moe {
+
+namespace {
+thread_local char g_last_error[512] = "";
+}
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+}
+
+moe_status_t fail(moe_status_t s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+moe_status_t check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+void set_max_dynamic_smem(const void* func, size_t bytes) {
+  static std::mutex mu;
+  static std::set<std::pair<int, const void*>> done;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return;
+  std::lock_guard<std::mutex> lk(mu);
+  if (done.insert({dev, func}).second)
+    (void)hipFuncSetAttribute(func, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+}
+
+namespace {
+
+bool valid_dt(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+bool valid_act(int a) { return a == MOE_ACT_GELU || a == MOE_ACT_SWIGLU; }
+
+moe_status_t check_route_args(const void* x, const void* w_r, int dt, int64_t T, int64_t d, int E, int k,
+                              const void* topk_idx, const void* topk_w, const void* logits) {
+  if (!valid_dt(dt)) return fail(MOE_EINVAL, "dtype %d is not MOE_F32 or MOE_BF16", dt);
+  if (T < 0 || T > (int64_t{1} << 31) - 1) return fail(MOE_EINVAL, "T=%lld out of range", (long long)T);
+  if (d < 1) return fail(MOE_EINVAL, "d=%lld must be >= 1", (long long)d);
+  if (E < 1 || E > kMaxExperts) return fail(MOE_EINVAL, "E=%d must be in [1, %d]", E, kMaxExperts);
+  if (k < 1 || k > E) return fail(MOE_EINVAL, "k=%d must be in [1, E=%d]", k, E);
+  if (T * k > (int64_t{1} << 31) - 1) return fail(MOE_EINVAL, "T*k exceeds 2^31-1");
+  if (T > 0 && (!x || !w_r || !topk_idx || !topk_w || !logits))
+    return fail(MOE_EINVAL, "moe_route: null required pointer");
+  if (T > 0 && (!aligned16(x) || !aligned16(w_r))) return fail(MOE_EINVAL, "x and w_r must be 16-byte aligned");
+  return MOE_OK;
+}
+
+moe_status_t check_ffn_args(const void* x, const int32_t* offsets, int G, int64_t max_rows, int64_t d,
+                            int64_t F, int act, int dt, const void* w_gate, const void* w_up,
+                            const void* w_down, const void* y) {
+  if (!valid_dt(dt)) return fail(MOE_EINVAL, "dtype %d is not MOE_F32 or MOE_BF16", dt);
+  if (!valid_act(act)) return fail(MOE_EINVAL, "activation %d is not GeLU or SwiGLU", act);
+  if (G < 1 || G > (1 << 20)) return fail(MOE_EINVAL, "G=%d out of range", G);
+  if (max_rows < 0 || max_rows > (int64_t{1} << 31) - 1) return fail(MOE_EINVAL, "max_rows out of range");
+  if (d < 1 || F < 1) return fail(MOE_EINVAL, "d and F must be >= 1");
+  if (dt == MOE_BF16 && (d % 64 != 0 || F % 64 != 0))
+    return fail(MOE_EUNSUPPORTED, "bf16 expert FFN needs d and F multiples of 64 (d=%lld F=%lld)",
+                (long long)d, (long long)F);
+  if (!x || !offsets || !w_gate || !w_down || !y) return fail(MOE_EINVAL, "moe_expert_ffn: null required pointer");
+  if (act == MOE_ACT_SWIGLU && !w_up) return fail(MOE_EINVAL, "SwiGLU needs w_up");
+  if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_down) || (w_up && !aligned16(w_up)) || !aligned16(y))
+    return fail(MOE_EINVAL, "x, weights and y must be 16-byte aligned");
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: unsupported shape";
+    case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace too small";
+    case MOE_EHIP: return "MOE_EHIP: HIP runtime error";
+  }
+  return "unknown moe_status_t";
+}
+
+const char* moe_last_error(void) { return g_last_error; }
+
+moe_status_t moe_route(const void* x, const void* w_r, const float* bias, moe_dtype_t dt, int64_t T, int64_t d,
+                       int32_t E, int32_t k, int32_t* topk_idx, float* topk_w, float* logits,
+                       hipStream_t stream) {
+  g_last_error[0] = 0;
+  if (moe_status_t st = check_route_args(x, w_r, dt, T, d, E, k, topk_idx, topk_w, logits)) return st;
+  return launch_route(x, w_r, bias, dt, T, d, E, k, topk_idx, topk_w, logits, stream);
+}
+
+size_t moe_dispatch_workspace_bytes(int64_t T, int32_t E) {
+  if (T < 0 || E < 1) return 0;
+  return dispatch_ws_bytes(T, E);
+}
+
+moe_status_t moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t E, int32_t k, int64_t capacity,
+                          int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* n_dropped,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_last_error[0] = 0;
+  if (T < 0 || T > (int64_t{1} << 31) - 1) return fail(MOE_EINVAL, "T out of range");
+  if (E < 1 || E > kMaxExperts) return fail(MOE_EINVAL, "E=%d must be in [1, %d]", E, kMaxExperts);
+  if (k < 1 || k > E) return fail(MOE_EINVAL, "k=%d must be in [1, E=%d]", k, E);
+  if (T * k > (int64_t{1} << 31) - 1) return fail(MOE_EINVAL, "T*k exceeds 2^31-1");
+  if (!counts || !offsets || !n_dropped || !ws || (T > 0 && (!topk_idx || !perm || !inv)))
+    return fail(MOE_EINVAL, "moe_dispatch: null required pointer");
+  const size_t need = dispatch_ws_bytes(T, E);
+  if (ws_bytes < need) return fail(MOE_EWORKSPACE, "dispatch needs %zu workspace bytes, got %zu", need, ws_bytes);
+  if (capacity > (int64_t{1} << 31) - 1) capacity = 0;   // larger than any count: unlimited
+  return launch_dispatch(topk_idx, T, E, k, capacity, counts, offsets, perm, inv, n_dropped, ws, stream);
+}
+
+size_t moe_expert_ffn_workspace_bytes(int64_t max_rows, int32_t G, int64_t d, int64_t F, moe_act_t act,
+                                      moe_dtype_t dt) {
+  if (max_rows < 0 || G < 1 || d < 1 || F < 1) return 0;
+  return ffn_plan(max_rows, G, false, d, F, act, dt).ws_bytes;
+}
+
+moe_status_t moe_expert_ffn(const void* x, const int32_t* perm, int32_t k, const int32_t* offsets, int32_t G,
+                            int64_t max_rows, int64_t d, int64_t F, moe_act_t act, moe_dtype_t dt,
+                            const void* w_gate, const void* w_up, const void* w_down, float* y, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  g_last_error[0] = 0;
+  if (moe_status_t st = check_ffn_args(x, offsets, G, max_rows, d, F, act, dt, w_gate, w_up, w_down, y)) return st;
+  if (perm && k < 1) return fail(MOE_EINVAL, "k must be >= 1 when perm is given");
+  const FfnPlan plan = ffn_plan(max_rows, G, false, d, F, act, dt);
+  if (!ws || ws_bytes < plan.ws_bytes)
+    return fail(MOE_EWORKSPACE, "expert FFN needs %zu workspace bytes, got %zu", plan.ws_bytes, ws_bytes);
+  FfnProblem p{};
+  p.x = x; p.perm = perm; p.k = k; p.offsets = offsets; p.G = G; p.max_rows = max_rows;
+  p.d = d; p.F = F; p.act = act; p.dt = dt;
+  p.w_gate = w_gate; p.w_up = act == MOE_ACT_SWIGLU ? w_up : nullptr; p.w_down = w_down;
+  return launch_ffn(p, plan, y, /*reduce_splits=*/true, ws, stream);
+}
+
+moe_status_t moe_combine(const float* y, int64_t y_rows, const int32_t* inv, const float* topk_w,
+                         const float* shared, int64_t T, int64_t d, int32_t k, moe_dtype_t out_dt, void* out,
+                         hipStream_t stream) {
+  g_last_error[0] = 0;
+  if (!valid_dt(out_dt)) return fail(MOE_EINVAL, "out dtype %d invalid", out_dt);
+  if (T < 0 || d < 1 || k < 1 || y_rows < 0) return fail(MOE_EINVAL, "bad sizes (T, d, k, y_rows)");
+  if (T > 0 && (!inv || !topk_w || !out || (y_rows > 0 && !y)))
+    return fail(MOE_EINVAL, "moe_combine: null required pointer");
+  return launch_combine(y, y_rows, 1, 0, inv, topk_w, shared, T, d, k, out_dt, out, stream);
+}
+
+static size_t layer_layout(const moe_layer_args_t* a, bool carve, WsCarver& c, int32_t** idx, float** w,
+                           float** logits, int32_t** counts, int32_t** offsets, int32_t** perm, int32_t** inv,
+                           int32_t** ndrop, void** dws, float** Y, void** fws, FfnPlan* plan) {
+  const int64_t T = a->T;
+  const bool shared = a->s_gate != nullptr;
+  const int64_t max_rows = T * a->k + (shared ? T : 0);
+  *plan = ffn_plan(max_rows, a->E, shared, a->d, a->F, a->act, a->dt);
+  float* lg = c.take<float>(static_cast<size_t>(T) * a->E);
+  int32_t* ix = c.take<int32_t>(static_cast<size_t>(T) * a->k);
+  float* tw = c.take<float>(static_cast<size_t>(T) * a->k);
+  int32_t* cn = c.take<int32_t>(a->E);
+  int32_t* of = c.take<int32_t>(a->E + 1);
+  int32_t* pm = c.take<int32_t>(static_cast<size_t>(T) * a->k);
+  int32_t* iv = c.take<int32_t>(static_cast<size_t>(T) * a->k);
+  int32_t* nd = c.take<int32_t>(1);
+  void* dw = c.take<char>(dispatch_ws_bytes(T, a->E));
+  float* yy = c.take<float>(static_cast<size_t>(plan->splits) * max_rows * a->d);
+  void* fw = c.take<char>(plan->ws_bytes);
+  if (carve) {
+    *logits = a->logits ? a->logits : lg;
+    *idx = a->topk_idx ? a->topk_idx : ix;
+    *w = a->topk_w ? a->topk_w : tw;
+    *counts = a->counts ? a->counts : cn;
+    *offsets = a->offsets ? a->offsets : of;
+    *perm = a->perm ? a->perm : pm;
+    *inv = a->inv ? a->inv : iv;
+    *ndrop = a->n_dropped ? a->n_dropped : nd;
+    *dws = dw;
+    *Y = yy;
+    *fws = fw;
+  }
+  return c.off;
+}
+
+size_t moe_layer_workspace_bytes(const moe_layer_args_t* a) {
+  if (!a || a->T < 0 || a->E < 1 || a->k < 1 || a->d < 1 || a->F < 1) return 0;
+  WsCarver c(nullptr);
+  int32_t *i, *cn, *of, *pm, *iv, *nd;
+  float *w, *lg, *Y;
+  void *dws, *fws;
+  FfnPlan plan;
+  return layer_layout(a, false, c, &i, &w, &lg, &cn, &of, &pm, &iv, &nd, &dws, &Y, &fws, &plan);
+}
+
+moe_status_t moe_layer_forward(const moe_layer_args_t* a, hipStream_t stream) {
+  g_last_error[0] = 0;
+  if (!a) return fail(MOE_EINVAL, "null args");
+  if (moe_status_t st = check_route_args(a->x, a->w_r, a->dt, a->T, a->d, a->E, a->k, a->x, a->x, a->x)) return st;
+  if (!valid_act(a->act)) return fail(MOE_EINVAL, "activation %d invalid", a->act);
+  if (!valid_dt(a->out_dt)) return fail(MOE_EINVAL, "out dtype %d invalid", a->out_dt);
+  if (a->F < 1) return fail(MOE_EINVAL, "F must be >= 1");
+  if (a->dt == MOE_BF16 && (a->d % 64 != 0 || a->F % 64 != 0))
+    return fail(MOE_EUNSUPPORTED, "bf16 layer needs d and F multiples of 64");
+  const bool swiglu = a->act == MOE_ACT_SWIGLU;
+  if (a->T > 0 && (!a->out || !a->w_gate || !a->w_down || (swiglu && !a->w_up)))
+    return fail(MOE_EINVAL, "moe_layer_forward: null required pointer");
+  if (a->s_gate && (!a->s_down || (swiglu && !a->s_up)))
+    return fail(MOE_EINVAL, "shared expert needs s_gate, s_down (and s_up for SwiGLU)");
+  const void* al[] = {a->w_gate, a->w_up, a->w_down, a->s_gate, a->s_up, a->s_down, a->out};
+  for (const void* p : al)
+    if (p && !aligned16(p)) return fail(MOE_EINVAL, "weights and out must be 16-byte aligned");
+  if (a->T == 0) return MOE_OK;
+  const size_t need = moe_layer_workspace_bytes(a);
+  if (!a->ws || a->ws_bytes < need)
+    return fail(MOE_EWORKSPACE, "layer needs %zu workspace bytes, got %zu", need, a->ws_bytes);
+  if (!aligned16(a->ws)) return fail(MOE_EINVAL, "workspace must be 16-byte aligned");
+
+  WsCarver c(a->ws);
+  int32_t *idx, *counts, *offsets, *perm, *inv, *ndrop;
+  float *w, *logits, *Y;
+  void *dws, *fws;
+  FfnPlan plan;
+  layer_layout(a, true, c, &idx, &w, &logits, &counts, &offsets, &perm, &inv, &ndrop, &dws, &Y, &fws, &plan);
+
+  const int64_t T = a->T;
+  const bool shared = a->s_gate != nullptr;
+  const int64_t max_rows = T * a->k + (shared ? T : 0);
+  int64_t capacity = a->capacity;
+  if (capacity > (int64_t{1} << 31) - 1) capacity = 0;
+
+  void* const* ev = a->stage_events;
+  auto mark = [&](int i) {
+    if (ev) (void)hipEventRecord(static_cast<hipEvent_t>(ev[i]), stream);
+  };
+  mark(0);
+  if (moe_status_t st = launch_route(a->x, a->w_r, a->bias, a->dt, T, a->d, a->E, a->k, idx, w, logits, stream))
+    return st;
+  mark(1);
+  if (moe_status_t st = launch_dispatch(idx, T, a->E, a->k, capacity, counts, offsets, perm, inv, ndrop, dws, stream))
+    return st;
+  mark(2);
+  FfnProblem p{};
+  p.x = a->x; p.perm = perm; p.k = a->k; p.offsets = offsets; p.G = a->E; p.max_rows = max_rows;
+  p.d = a->d; p.F = a->F; p.act = a->act; p.dt = a->dt;
+  p.w_gate = a->w_gate; p.w_up = swiglu ? a->w_up : nullptr; p.w_down = a->w_down;
+  p.s_gate = a->s_gate; p.s_up = swiglu ? a->s_up : nullptr; p.s_down = a->s_down;
+  p.shared_rows = shared ? T : 0;
+  p.shared_row0 = T * a->k;
+  if (moe_status_t st = launch_ffn(p, plan, Y, /*reduce_splits=*/false, fws, stream, ev ? ev + 3 : nullptr))
+    return st;
+  const float* sh = shared ? Y + T * a->k * a->d : nullptr;
+  if (moe_status_t st = launch_combine(Y, T * a->k, plan.splits, max_rows * a->d, inv, w, sh, T, a->d, a->k,
+                                       a->out_dt, a->out, stream))
+    return st;
+  mark(6);
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,103 @@
+// Internal helpers shared by the HIP translation units of libmoe (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMaxExperts = 1024;
+
+// ---- host-side status handling -------------------------------------------------
+void set_error(const char* fmt, ...);
+moe_status_t fail(moe_status_t s, const char* fmt, ...);
+moe_status_t check_launch(const char* what);
+// Raise a kernel's dynamic-LDS limit once per (device, kernel).
+void set_max_dynamic_smem(const void* func, size_t bytes);
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Bump allocator over a caller-provided workspace (host arithmetic only).
+struct WsCarver {
+  char* base;
+  size_t off = 0;
+  explicit WsCarver(void* b) : base(static_cast<char*>(b)) {}
+  template <typename T>
+  T* take(size_t n) {
+    off = align_up(off, 256);
+    T* p = reinterpret_cast<T*>(base ? base + off : nullptr);
+    off += n * sizeof(T);
+    return p;
+  }
+};
+
+// ---- internal launchers shared between entry points ----------------------------
+moe_status_t launch_route(const void* x, const void* w_r, const float* bias, int dt,
+                          int64_t T, int64_t d, int E, int k, int32_t* topk_idx,
+                          float* topk_w, float* logits, hipStream_t s);
+
+size_t dispatch_ws_bytes(int64_t T, int E);
+moe_status_t launch_dispatch(const int32_t* topk_idx, int64_t T, int E, int k, int64_t capacity,
+                             int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                             int32_t* n_dropped, void* ws, hipStream_t s);
+
+// One FFN problem: G routed groups (rows from `offsets`, gathered through `perm`)
+// plus an optional shared group of `shared_rows` identity rows placed at row
+// `shared_row0` of the output.
+struct FfnProblem {
+  const void* x;
+  const int32_t* perm;      // nullable
+  int k;                    // divisor for perm entries
+  const int32_t* offsets;   // [G+1] device
+  int G;
+  int64_t max_rows;         // rows of y / H allocated
+  int64_t d, F;
+  int act, dt;
+  const void* w_gate; const void* w_up; const void* w_down;       // [G, ...]
+  const void* s_gate; const void* s_up; const void* s_down;       // shared or null
+  int64_t shared_rows;      // 0 = no shared group
+  int64_t shared_row0;
+};
+
+struct FfnPlan {
+  int splits;               // split-K factor of the down projection
+  int64_t max_mtiles;
+  size_t ws_bytes;
+};
+FfnPlan ffn_plan(int64_t max_rows, int G, bool has_shared, int64_t d, int64_t F, int act, int dt);
+// y: [splits][max_rows][d] fp32 partial sums when plan.splits > 1 and reduce_splits is
+// false; otherwise [max_rows][d] final.
+// ev (nullable): events recorded after the schedule, up-projection and down-projection.
+moe_status_t launch_ffn(const FfnProblem& p, const FfnPlan& plan, float* y, bool reduce_splits,
+                        void* ws, hipStream_t s, void* const* ev = nullptr);
+
+moe_status_t launch_combine(const float* y, int64_t y_rows, int nsplit, int64_t split_stride,
+                            const int32_t* inv, const float* topk_w, const float* shared,
+                            int64_t T, int64_t d, int k, int out_dt, void* out, hipStream_t s);
+
+// ---- device helpers ----------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+// Round-to-nearest-even fp32 -> bf16 (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float silu_f(float v) { return v / (1.0f + __expf(-v)); }
+__device__ __forceinline__ float gelu_f(float v) { return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f)); }
+
+}  // namespace moe

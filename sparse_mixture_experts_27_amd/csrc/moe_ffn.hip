@@ -1,0 +1,536 @@
+// Grouped expert FFN.  [cnnet] "MoE混合专家架构原理与工程实践…": expert weights stacked in
+// one tensor and sliced by index, the tokens of one expert computed together;
+// [200B-5] "四个专家同时算…": the vectors bound for one expert are batched.
+//
+// Each group (expert) owns a contiguous range of rows of the expert-sorted order.
+// Two grouped GEMMs, both C[m, n] = sum_k A[m, k] B[n, k] with K-contiguous operands:
+//   up:   A = x rows gathered through the permutation, B = W_gate (and W_up) [F, d];
+//         epilogue silu(g) * u (SwiGLU) or gelu(g), rounded once to bf16 -> H [rows, F]
+//   down: A = H rows, B = W_down [d, F] -> y [rows, d] fp32 (optionally split over K)
+// A device-side schedule (one tiny kernel) turns the group offsets into M-tiles, so
+// no host synchronisation is needed to learn how many rows each expert received.
+//
+// bf16 tile: 256 rows x 256 MFMA columns x 64 K per stage, 4 waves.  Wave w owns 64
+// columns of every row of the tile: its weight fragments are private to it and are
+// loaded straight from global memory into registers in the MFMA operand layout (no
+// LDS), while the activation tile is shared by the 4 waves through LDS (double-
+// buffered, 16-byte chunks XOR-swizzled by row).  Only the 16-row fragments that hold
+// real rows are multiplied, so a group with 70 rows costs 5 fragments, not 16.
+// Workgroups are remapped so that each XCD (blockIdx % 8) walks a contiguous range of
+// tiles: the tiles of one expert share its activation rows in that XCD's L2.
+#include "moe_common.h"
+
+namespace moe {
+namespace {
+
+constexpr int BM = 256;          // rows per M-tile (bf16)
+constexpr int BK = 64;           // K per pipeline stage
+constexpr int BM_F32 = 64;       // rows per M-tile (fp32 path)
+
+enum GemmMode { MODE_SWIGLU_UP = 0, MODE_GELU_UP = 1, MODE_DOWN = 2 };
+
+// Schedule layout (int32 words in the workspace):
+//   [0] total M-tiles, [1 .. Gt+1] exclusive prefix of M-tiles per group,
+//   then row0[Gt], rows[Gt].
+struct SchedView {
+  const int32_t* base;
+  int Gt;
+  __device__ int32_t total() const { return base[0]; }
+  __device__ const int32_t* prefix() const { return base + 1; }
+  __device__ const int32_t* row0() const { return base + 2 + Gt; }
+  __device__ const int32_t* rows() const { return base + 2 + 2 * Gt; }
+};
+
+inline size_t sched_words(int Gt) { return 2 + 3 * static_cast<size_t>(Gt); }
+
+__global__ __launch_bounds__(1024) void ffn_schedule_kernel(const int32_t* __restrict__ offsets, int G,
+                                                            int64_t max_rows, int64_t shared_rows,
+                                                            int64_t shared_row0, int bm,
+                                                            int32_t* __restrict__ sched) {
+  __shared__ int32_t wsum[16];
+  const int Gt = G + (shared_rows > 0 ? 1 : 0);
+  int32_t* prefix = sched + 1;
+  int32_t* row0 = sched + 2 + Gt;
+  int32_t* rows = sched + 2 + 2 * Gt;
+  int32_t carry = 0;
+  for (int g0 = 0; g0 < Gt; g0 += 1024) {
+    const int g = g0 + threadIdx.x;
+    int32_t mt = 0;
+    if (g < Gt) {
+      int64_t r0, r1;
+      if (g < G) {
+        r0 = offsets[g];
+        r1 = offsets[g + 1];
+        r0 = r0 < 0 ? 0 : (r0 > max_rows ? max_rows : r0);
+        r1 = r1 < r0 ? r0 : (r1 > max_rows ? max_rows : r1);
+      } else {
+        r0 = shared_row0;
+        r1 = shared_row0 + shared_rows;
+      }
+      row0[g] = static_cast<int32_t>(r0);
+      rows[g] = static_cast<int32_t>(r1 - r0);
+      mt = static_cast<int32_t>((r1 - r0 + bm - 1) / bm);
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int32_t v = mt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int32_t o = __shfl_up(v, off);
+      if (lane >= off) v += o;
+    }
+    if (lane == 63) wsum[wave] = v;
+    __syncthreads();
+    int32_t before = carry, all = carry;
+    for (int w = 0; w < 16; ++w) {
+      if (w < wave) before += wsum[w];
+      all += wsum[w];
+    }
+    if (g < Gt) prefix[g] = before + v - mt;
+    carry = all;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    prefix[Gt] = carry;
+    sched[0] = carry;
+  }
+}
+
+struct GemmArgs {
+  const uint16_t* a;        // x [n_x, K] (up) or H [rows, K] (down); fp32 data for the fp32 path
+  const int32_t* perm;      // up only: nullable
+  int k_div;                // perm entries divided by this give the token
+  const void* w0;           // gate / W1 / Wd, stacked [G, N_w, K]
+  const void* w1;           // up (SwiGLU) or null
+  const void* sw0;          // shared-group weights
+  const void* sw1;
+  const int32_t* sched;
+  int G, Gt;
+  int64_t shared_row0;
+  int64_t K, N;             // contraction and output width (F for up, d for down)
+  int nt;                   // N-tiles per M-tile
+  int splits;               // K splits (down only)
+  int64_t k_chunk;          // K per split (multiple of BK)
+  void* out;                // H (bf16 or f32) or y / partials (f32)
+  int64_t split_stride;     // elements between split partial buffers
+};
+
+// Locate the logical tile: group, M-tile, N-tile, split.
+struct TileInfo {
+  int g;
+  int64_t row_begin;
+  int nrows;
+  int ntile;
+  int split;
+};
+
+__device__ __forceinline__ bool decode_tile(const GemmArgs& p, int bm, TileInfo& ti) {
+  const SchedView sv{p.sched, p.Gt};
+  const int64_t nts = static_cast<int64_t>(p.nt) * p.splits;
+  const int64_t n_active = static_cast<int64_t>(sv.total()) * nts;
+  const int64_t per_xcd = (n_active + 7) / 8;
+  const int64_t b = blockIdx.x;
+  const int64_t slot = b >> 3;
+  if (slot >= per_xcd) return false;
+  const int64_t L = (b & 7) * per_xcd + slot;
+  if (L >= n_active) return false;
+  // largest g with prefix[g] * nts <= L (prefix is non-decreasing)
+  const int32_t* pre = sv.prefix();
+  int lo = 0, hi = p.Gt;          // invariant: prefix[lo]*nts <= L < prefix[hi]*nts
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (static_cast<int64_t>(pre[mid]) * nts <= L) lo = mid; else hi = mid;
+  }
+  const int g = lo;
+  const int64_t local = L - static_cast<int64_t>(pre[g]) * nts;
+  const int mt = pre[g + 1] - pre[g];
+  const int64_t j = local / mt;
+  const int m = static_cast<int>(local - j * mt);
+  ti.g = g;
+  ti.ntile = static_cast<int>(j / p.splits);
+  ti.split = static_cast<int>(j - static_cast<int64_t>(ti.ntile) * p.splits);
+  ti.row_begin = static_cast<int64_t>(sv.row0()[g]) + static_cast<int64_t>(m) * bm;
+  const int rem = sv.rows()[g] - m * bm;
+  ti.nrows = rem < bm ? rem : bm;
+  return true;
+}
+
+// Source row of the A operand for output row r of group g.
+__device__ __forceinline__ int64_t a_source_row(const GemmArgs& p, int mode, int g, int64_t r) {
+  if (mode == MODE_DOWN) return r;
+  if (g >= p.G) return r - p.shared_row0;           // shared group: identity rows
+  return p.perm ? static_cast<int64_t>(p.perm[r] / p.k_div) : r;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256, 1) void ffn_gemm_bf16_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * BK];   // 2 x 32 KB
+  TileInfo ti;
+  if (!decode_tile(p, BM, ti)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nrows16 = (ti.nrows + 15) & ~15;
+  const int nmf = nrows16 >> 4;
+
+  // ---- K range of this tile
+  int64_t k_begin = 0, k_end = p.K;
+  if (MODE == MODE_DOWN && p.splits > 1) {
+    k_begin = static_cast<int64_t>(ti.split) * p.k_chunk;
+    k_end = k_begin + p.k_chunk < p.K ? k_begin + p.k_chunk : p.K;
+  }
+  const int nst = static_cast<int>((k_end - k_begin) / BK);
+
+  // ---- weight rows (columns of C) owned by this wave
+  const bool shared_grp = ti.g >= p.G;
+  const uint16_t* W0 = static_cast<const uint16_t*>(shared_grp ? p.sw0 : p.w0);
+  const uint16_t* W1 = static_cast<const uint16_t*>(shared_grp ? p.sw1 : p.w1);
+  const int64_t wstride = shared_grp ? 0 : static_cast<int64_t>(ti.g) * p.N * p.K;
+  int64_t col_base;                         // first output column of this wave
+  if (MODE == MODE_SWIGLU_UP) col_base = static_cast<int64_t>(ti.ntile) * 128 + wave * 32;
+  else col_base = static_cast<int64_t>(ti.ntile) * 256 + wave * 64;
+  const bool wave_on = col_base < p.N;
+  const uint16_t* bptr[4];
+#pragma unroll
+  for (int nf = 0; nf < 4; ++nf) {
+    int64_t wrow;
+    const uint16_t* Wm;
+    if (MODE == MODE_SWIGLU_UP) {
+      wrow = col_base + (nf & 1) * 16 + (lane & 15);
+      Wm = (nf < 2) ? W0 : W1;
+    } else {
+      wrow = col_base + nf * 16 + (lane & 15);
+      Wm = W0;
+    }
+    if (!wave_on) wrow = 0;
+    bptr[nf] = Wm + wstride + wrow * p.K + k_begin + 8 * (lane >> 4);
+  }
+
+  // ---- activation rows loaded by this thread: rows i*32 + tid/8, 16-byte chunk tid%8
+  const int chunk = tid & 7;
+  int64_t arow[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = i * 32 + (tid >> 3);
+    arow[i] = (r < ti.nrows) ? a_source_row(p, MODE, ti.g, ti.row_begin + r) : -1;
+  }
+  const uint16_t* A = p.a;
+
+  u32x4 ra[8];
+  bf16x8 rb[2][2][4];      // [buffer][k32 step][fragment]
+
+  auto load_a = [&](int st) {
+    const int64_t k0 = k_begin + static_cast<int64_t>(st) * BK + chunk * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i * 32 < nrows16) {
+        if (arow[i] >= 0) ra[i] = *reinterpret_cast<const u32x4*>(A + arow[i] * p.K + k0);
+        else ra[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = i * 32 + (tid >> 3);
+      if (i * 32 < nrows16 && r < nrows16)
+        *reinterpret_cast<u32x4*>(&As[buf][r * BK + ((chunk ^ (r & 7)) * 8)]) = ra[i];
+    }
+  };
+  auto load_b = [&](int st, int buf) {
+    if (!wave_on) return;
+    const int64_t ko = static_cast<int64_t>(st) * BK;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int nf = 0; nf < 4; ++nf)
+        rb[buf][s][nf] = *reinterpret_cast<const bf16x8*>(bptr[nf] + ko + s * 32);
+  };
+
+  f32x4 acc[16][4];
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int abuf, int bbuf) {
+    if (!wave_on) return;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int mf = 0; mf < 16; ++mf) {
+        if (mf < nmf) {
+          const int r = mf * 16 + (lane & 15);
+          const int c = (s * 4 + (lane >> 4)) ^ (r & 7);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&As[abuf][r * BK + c * 8]);
+#pragma unroll
+          for (int nf = 0; nf < 4; ++nf)
+            acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, rb[bbuf][s][nf], acc[mf][nf], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  if (nst > 0) {
+    load_a(0);
+    load_b(0, 0);
+    store_a(0);
+    __syncthreads();
+    for (int st = 0; st < nst; st += 2) {
+      // even stage: compute buffer 0 while stage st+1 is in flight
+      const bool more1 = st + 1 < nst;
+      if (more1) { load_a(st + 1); load_b(st + 1, 1); }
+      compute(0, 0);
+      if (more1) store_a(1);
+      __syncthreads();
+      if (!more1) break;
+      const bool more2 = st + 2 < nst;
+      if (more2) { load_a(st + 2); load_b(st + 2, 0); }
+      compute(1, 1);
+      if (more2) store_a(0);
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue.  C layout: lane holds rows 4*(lane/16)+v of each 16x16 block, column lane%16.
+  if (!wave_on) return;
+#pragma unroll
+  for (int mf = 0; mf < 16; ++mf) {
+    if (mf < nmf) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = mf * 16 + 4 * (lane >> 4) + v;
+        if (r < ti.nrows) {
+          const int64_t orow = ti.row_begin + r;
+          if (MODE == MODE_SWIGLU_UP) {
+            uint16_t* H = static_cast<uint16_t*>(p.out);
+#pragma unroll
+            for (int nf = 0; nf < 2; ++nf) {
+              const int64_t f = col_base + nf * 16 + (lane & 15);
+              const float h = silu_f(acc[mf][nf][v]) * acc[mf][nf + 2][v];
+              H[orow * p.N + f] = f32_to_bf16(h);
+            }
+          } else if (MODE == MODE_GELU_UP) {
+            uint16_t* H = static_cast<uint16_t*>(p.out);
+#pragma unroll
+            for (int nf = 0; nf < 4; ++nf) {
+              const int64_t f = col_base + nf * 16 + (lane & 15);
+              H[orow * p.N + f] = f32_to_bf16(gelu_f(acc[mf][nf][v]));
+            }
+          } else {
+            float* Y = static_cast<float*>(p.out) + static_cast<int64_t>(ti.split) * p.split_stride;
+#pragma unroll
+            for (int nf = 0; nf < 4; ++nf) {
+              const int64_t n = col_base + nf * 16 + (lane & 15);
+              Y[orow * p.N + n] = acc[mf][nf][v];
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---- fp32 path: 64 x 64 output tile, 256 threads x (4 x 4), K staged 16 at a time.
+template <int MODE>
+__global__ __launch_bounds__(256) void ffn_gemm_f32_kernel(GemmArgs p) {
+  constexpr int TN = 64, TK = 16;
+  __shared__ float As[TK][BM_F32 + 1];
+  __shared__ float Bs0[TK][TN + 1];
+  __shared__ float Bs1[TK][TN + 1];
+  TileInfo ti;
+  if (!decode_tile(p, BM_F32, ti)) return;
+  const int tid = threadIdx.x;
+  const int tr = tid / 16, tc = tid % 16;        // 16 x 16 threads, 4 x 4 outputs each
+  const bool shared_grp = ti.g >= p.G;
+  const float* W0 = static_cast<const float*>(shared_grp ? p.sw0 : p.w0);
+  const float* W1 = static_cast<const float*>(shared_grp ? p.sw1 : p.w1);
+  const int64_t wstride = shared_grp ? 0 : static_cast<int64_t>(ti.g) * p.N * p.K;
+  const int64_t n0 = static_cast<int64_t>(ti.ntile) * TN;
+  const float* A = reinterpret_cast<const float*>(p.a);
+  float acc0[4][4] = {}, acc1[4][4] = {};
+  // loader mapping: 64 rows x 16 k = 1024 values, 4 per thread
+  for (int64_t k0 = 0; k0 < p.K; k0 += TK) {
+    for (int i = tid; i < BM_F32 * TK; i += 256) {
+      const int r = i / TK, kk = i % TK;
+      float v = 0.f;
+      if (r < ti.nrows && k0 + kk < p.K)
+        v = A[a_source_row(p, MODE, ti.g, ti.row_begin + r) * p.K + k0 + kk];
+      As[kk][r] = v;
+      const int64_t n = n0 + r;
+      float b0 = 0.f, b1 = 0.f;
+      if (n < p.N && k0 + kk < p.K) {
+        b0 = W0[wstride + n * p.K + k0 + kk];
+        if (MODE == MODE_SWIGLU_UP) b1 = W1[wstride + n * p.K + k0 + kk];
+      }
+      Bs0[kk][r] = b0;
+      Bs1[kk][r] = b1;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < TK; ++kk) {
+      float a[4], b0[4], b1[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { a[i] = As[kk][tr * 4 + i]; b0[i] = Bs0[kk][tc * 4 + i]; b1[i] = Bs1[kk][tc * 4 + i]; }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc0[i][j] = fmaf(a[i], b0[j], acc0[i][j]);
+          if (MODE == MODE_SWIGLU_UP) acc1[i][j] = fmaf(a[i], b1[j], acc1[i][j]);
+        }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = tr * 4 + i;
+    if (r >= ti.nrows) continue;
+    const int64_t orow = ti.row_begin + r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t n = n0 + tc * 4 + j;
+      if (n >= p.N) continue;
+      float v;
+      if (MODE == MODE_SWIGLU_UP) v = silu_f(acc0[i][j]) * acc1[i][j];
+      else if (MODE == MODE_GELU_UP) v = gelu_f(acc0[i][j]);
+      else v = acc0[i][j];
+      static_cast<float*>(p.out)[orow * p.N + n] = v;
+    }
+  }
+}
+
+// Sum the split-K partial buffers into y for the rows that belong to some group.
+__global__ __launch_bounds__(256) void ffn_reduce_splits_kernel(const float* __restrict__ part, int splits,
+                                                                int64_t split_stride, const int32_t* __restrict__ offsets,
+                                                                int G, int64_t max_rows, int64_t d,
+                                                                float* __restrict__ y) {
+  int64_t r0 = offsets[0], r1 = offsets[G];
+  r0 = r0 < 0 ? 0 : r0;
+  r1 = r1 > max_rows ? max_rows : r1;
+  const int64_t n4 = d / 4;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < (r1 - r0) * n4;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t r = r0 + i / n4, c = (i % n4) * 4;
+    f32x4 s = *reinterpret_cast<const f32x4*>(part + r * d + c);
+    for (int sp = 1; sp < splits; ++sp) s += *reinterpret_cast<const f32x4*>(part + sp * split_stride + r * d + c);
+    *reinterpret_cast<f32x4*>(y + r * d + c) = s;
+  }
+}
+
+}  // namespace
+
+FfnPlan ffn_plan(int64_t max_rows, int G, bool has_shared, int64_t d, int64_t F, int act, int dt) {
+  FfnPlan pl{};
+  const int bm = dt == MOE_BF16 ? BM : BM_F32;
+  (void)act;
+  const int Gt = G + (has_shared ? 1 : 0);
+  pl.max_mtiles = (max_rows + bm - 1) / bm + Gt + 1;
+  pl.splits = 1;
+  if (dt == MOE_BF16) {
+    const int64_t nt2 = (d + 255) / 256;
+    int64_t est = (max_rows + bm - 1) / bm;
+    const int64_t busy = G < max_rows ? G : max_rows;
+    if (busy > est) est = busy;
+    while (est * nt2 * pl.splits < 2048 && F / (BK * pl.splits * 2) >= 8) pl.splits *= 2;
+  }
+  const size_t elem = dt == MOE_BF16 ? 2 : 4;
+  size_t ws = align_up(sched_words(Gt) * sizeof(int32_t), 256);
+  ws += align_up(static_cast<size_t>(max_rows) * F * elem, 256);                       // H
+  if (pl.splits > 1) ws += align_up(static_cast<size_t>(pl.splits) * max_rows * d * 4, 256);  // partials
+  pl.ws_bytes = ws;
+  return pl;
+}
+
+moe_status_t launch_ffn(const FfnProblem& p, const FfnPlan& plan, float* y, bool reduce_splits,
+                        void* ws, hipStream_t s, void* const* ev) {
+  auto mark = [&](int i) {
+    if (ev) (void)hipEventRecord(static_cast<hipEvent_t>(ev[i]), s);
+  };
+  const bool has_shared = p.shared_rows > 0;
+  const int Gt = p.G + (has_shared ? 1 : 0);
+  const bool bf = p.dt == MOE_BF16;
+  const int bm = bf ? BM : BM_F32;
+  WsCarver c(ws);
+  int32_t* sched = c.take<int32_t>(sched_words(Gt));
+  void* H = bf ? static_cast<void*>(c.take<uint16_t>(static_cast<size_t>(p.max_rows) * p.F))
+               : static_cast<void*>(c.take<float>(static_cast<size_t>(p.max_rows) * p.F));
+  float* part = nullptr;
+  if (plan.splits > 1) part = c.take<float>(static_cast<size_t>(plan.splits) * p.max_rows * p.d);
+  if (Gt == 0 || p.max_rows == 0) {
+    mark(0); mark(1); mark(2);
+    return MOE_OK;
+  }
+
+  ffn_schedule_kernel<<<1, 1024, 0, s>>>(p.offsets, p.G, p.max_rows, p.shared_rows, p.shared_row0, bm, sched);
+  if (moe_status_t st = check_launch("ffn schedule kernel")) return st;
+  mark(0);
+
+  GemmArgs g{};
+  g.perm = p.perm;
+  g.k_div = p.k > 0 ? p.k : 1;
+  g.sched = sched;
+  g.G = p.G;
+  g.Gt = Gt;
+  g.shared_row0 = p.shared_row0;
+  g.splits = 1;
+  g.split_stride = 0;
+
+  // ---- up projection: H = act(x W_gate^T) [* (x W_up^T)]
+  const bool swiglu = p.act == MOE_ACT_SWIGLU;
+  g.a = static_cast<const uint16_t*>(p.x);
+  g.w0 = p.w_gate;
+  g.w1 = swiglu ? p.w_up : nullptr;
+  g.sw0 = p.s_gate;
+  g.sw1 = swiglu ? p.s_up : nullptr;
+  g.K = p.d;
+  g.N = p.F;
+  g.k_chunk = p.d;
+  g.out = H;
+  if (bf) {
+    g.nt = static_cast<int>(swiglu ? (p.F + 127) / 128 : (p.F + 255) / 256);
+    const int64_t grid = ((plan.max_mtiles * g.nt + 7) / 8) * 8;
+    if (swiglu) ffn_gemm_bf16_kernel<MODE_SWIGLU_UP><<<static_cast<unsigned>(grid), 256, 0, s>>>(g);
+    else ffn_gemm_bf16_kernel<MODE_GELU_UP><<<static_cast<unsigned>(grid), 256, 0, s>>>(g);
+  } else {
+    g.nt = static_cast<int>((p.F + 63) / 64);
+    const int64_t grid = ((plan.max_mtiles * g.nt + 7) / 8) * 8;
+    if (swiglu) ffn_gemm_f32_kernel<MODE_SWIGLU_UP><<<static_cast<unsigned>(grid), 256, 0, s>>>(g);
+    else ffn_gemm_f32_kernel<MODE_GELU_UP><<<static_cast<unsigned>(grid), 256, 0, s>>>(g);
+  }
+  if (moe_status_t st = check_launch("ffn up-projection kernel")) return st;
+  mark(1);
+
+  // ---- down projection: y = H W_down^T
+  g.a = static_cast<const uint16_t*>(H);
+  g.perm = nullptr;
+  g.w0 = p.w_down;
+  g.w1 = nullptr;
+  g.sw0 = p.s_down;
+  g.sw1 = nullptr;
+  g.K = p.F;
+  g.N = p.d;
+  if (bf) {
+    g.nt = static_cast<int>((p.d + 255) / 256);
+    g.splits = plan.splits;
+    g.k_chunk = ((p.F / BK + plan.splits - 1) / plan.splits) * BK;
+    g.split_stride = p.max_rows * p.d;
+    g.out = plan.splits > 1 && reduce_splits ? static_cast<void*>(part) : static_cast<void*>(y);
+    const int64_t grid = ((plan.max_mtiles * g.nt * g.splits + 7) / 8) * 8;
+    ffn_gemm_bf16_kernel<MODE_DOWN><<<static_cast<unsigned>(grid), 256, 0, s>>>(g);
+  } else {
+    g.nt = static_cast<int>((p.d + 63) / 64);
+    g.k_chunk = p.F;
+    g.out = y;
+    const int64_t grid = ((plan.max_mtiles * g.nt + 7) / 8) * 8;
+    ffn_gemm_f32_kernel<MODE_DOWN><<<static_cast<unsigned>(grid), 256, 0, s>>>(g);
+  }
+  if (moe_status_t st = check_launch("ffn down-projection kernel")) return st;
+  mark(2);
+
+  if (bf && plan.splits > 1 && reduce_splits) {
+    ffn_reduce_splits_kernel<<<1024, 256, 0, s>>>(part, plan.splits, p.max_rows * p.d, p.offsets, p.G,
+                                                   p.max_rows, p.d, y);
+    if (moe_status_t st = check_launch("ffn split reduction kernel")) return st;
+  }
+  return MOE_OK;
+}
+
+}  // namespace moe

@@ -1,0 +1,244 @@
+// Router: logits z = x W_r (+ b), top-k with lowest-index tie-break, renormalised
+// weights.  [mlqm] www.mlqm.cn/news/130088 §3.1 (logits = h W_r, softmax, top-k) and
+// §3.3 (w_i = p_i / (p_i + p_j)); [200B-5] "谁来决定请哪几个专家？" (top-k).
+//
+// One workgroup (4 waves) owns 16 tokens.  bf16: the router GEMM runs on
+// v_mfma_f32_16x16x32_bf16 with W_r staged through LDS transposed to [expert][k];
+// each wave takes a quarter of every 256-wide K chunk and the four partial sums are
+// added in a fixed order, so the logits are bit-reproducible.  fp32: plain FMA.
+// The top-k epilogue runs one wave per token on a 64-bit key (ordered logit, inverted
+// expert index): the largest key is the largest logit, ties going to the lowest index.
+#include "moe_common.h"
+
+namespace moe {
+namespace {
+
+constexpr int RT_TOK = 16;     // tokens per workgroup
+constexpr int RT_KC = 256;     // K chunk per iteration (4 waves x 64)
+constexpr int RT_EB = 64;      // experts per pass of the GEMM
+constexpr int RT_PITCH = RT_KC + 8;   // LDS row pitch (elements) of the transposed W_r chunk
+
+// Dynamic LDS layout; the logit rows are sized by E, so E <= 64 stays under 64 KB.
+struct RouteSmem {
+  uint16_t (*wt)[RT_PITCH];   // [RT_EB][RT_PITCH]  W_r chunk, [expert][k]   (bf16 path)
+  float (*red)[RT_TOK][RT_EB];// [4][RT_TOK][RT_EB] per-wave partial logits (bf16 path)
+  float* z;                   // [RT_TOK][E]        final logits of the 16 tokens
+  float* zs;                  // [4][E]             selected logits, one row per wave
+  __device__ RouteSmem(char* base, int E, bool gemm) {
+    size_t off = 0;
+    if (gemm) {
+      wt = reinterpret_cast<uint16_t(*)[RT_PITCH]>(base);
+      off += sizeof(uint16_t) * RT_EB * RT_PITCH;
+      red = reinterpret_cast<float(*)[RT_TOK][RT_EB]>(base + off);
+      off += sizeof(float) * 4 * RT_TOK * RT_EB;
+    }
+    z = reinterpret_cast<float*>(base + off);
+    off += sizeof(float) * RT_TOK * E;
+    zs = reinterpret_cast<float*>(base + off);
+  }
+};
+
+inline size_t route_smem_bytes(int E, bool gemm) {
+  size_t b = sizeof(float) * (RT_TOK + 4) * static_cast<size_t>(E);
+  if (gemm) b += sizeof(uint16_t) * RT_EB * RT_PITCH + sizeof(float) * 4 * RT_TOK * RT_EB;
+  return b;
+}
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(const uint16_t v[8]) {
+  u32x4 q;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] = static_cast<uint32_t>(v[2 * i]) | (static_cast<uint32_t>(v[2 * i + 1]) << 16);
+  return __builtin_bit_cast(bf16x8, q);
+}
+
+__device__ __forceinline__ uint32_t ordered_key(float z) {
+  uint32_t b = __float_as_uint(z);
+  if (b == 0x80000000u) b = 0u;                       // -0 ties with +0
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key_to_float(uint32_t o) {
+  uint32_t b = (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o;
+  return __uint_as_float(b);
+}
+
+// Top-k of one token's logits zrow[0..E) by one wave; writes idx/w rows.  zs is this
+// wave's LDS row for the selected logits.
+__device__ void topk_one_token(const float* zrow, float* zs, int E, int k, int32_t* idx_out,
+                               float* w_out) {
+  const int lane = threadIdx.x & 63;
+  const int per_lane = (E + 63) / 64;      // <= 16
+  uint32_t removed = 0;
+  for (int j = 0; j < k; ++j) {
+    // best remaining candidate of this lane
+    uint32_t bhi = 0, blo = 0;
+    for (int i = 0; i < per_lane; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E && !((removed >> i) & 1u)) {
+        const uint32_t hi = ordered_key(zrow[e]);
+        const uint32_t lo = 0xffffffffu - static_cast<uint32_t>(e);
+        if (hi > bhi || (hi == bhi && lo > blo)) { bhi = hi; blo = lo; }
+      }
+    }
+    // wave-wide max of the 64-bit key (hi, lo)
+    uint32_t mhi = bhi, mlo = blo;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const uint32_t ohi = __shfl_xor(mhi, off);
+      const uint32_t olo = __shfl_xor(mlo, off);
+      if (ohi > mhi || (ohi == mhi && olo > mlo)) { mhi = ohi; mlo = olo; }
+    }
+    const int e_win = static_cast<int>(0xffffffffu - mlo);
+    if ((e_win & 63) == lane) removed |= 1u << (e_win >> 6);
+    if (lane == 0) { idx_out[j] = e_win; zs[j] = key_to_float(mhi); }
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  // w_j = exp(z_j - z_0) / sum_i exp(z_i - z_0); fixed butterfly order
+  const float z0 = zs[0];
+  float part = 0.f;
+  for (int j = lane; j < k; j += 64) part += expf(zs[j] - z0);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+  const float inv = 1.0f / part;
+  for (int j = lane; j < k; j += 64) w_out[j] = expf(zs[j] - z0) * inv;
+  __builtin_amdgcn_wave_barrier();
+}
+
+__device__ void finish_tokens(RouteSmem& sm, int64_t tok0, int64_t T, int E, int k,
+                              int32_t* topk_idx, float* topk_w) {
+  const int wave = threadIdx.x >> 6;
+  for (int t = wave; t < RT_TOK; t += 4) {
+    const int64_t tok = tok0 + t;
+    if (tok < T) topk_one_token(sm.z + t * E, sm.zs + wave * E, E, k, topk_idx + tok * k, topk_w + tok * k);
+  }
+}
+
+__global__ __launch_bounds__(256) void route_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_r, const float* __restrict__ bias,
+    int64_t T, int64_t d, int E, int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    float* __restrict__ logits) {
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  RouteSmem sm(smem_raw, E, true);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * RT_TOK;
+  const int64_t my_tok = tok0 + (lane & 15);
+  const bool tok_ok = my_tok < T;
+  const uint16_t* xrow = x + (tok_ok ? my_tok : 0) * d;
+  const bool vec_w = (E % 8) == 0;
+  const bool vec_x = (d % 8) == 0;
+
+  for (int e0 = 0; e0 < E; e0 += RT_EB) {
+    f32x4 acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int64_t k0 = 0; k0 < d; k0 += RT_KC) {
+      __syncthreads();   // previous chunk fully consumed
+      // stage W_r[k0 : k0+256, e0 : e0+64] transposed into sm.wt[e][k]
+      for (int p = 0; p < RT_KC / 32; ++p) {
+        const int row = p * 32 + (tid >> 3);
+        const int ec = (tid & 7) * 8;
+        const int64_t kk = k0 + row;
+        uint16_t v[8];
+        if (vec_w && kk < d && e0 + ec + 8 <= E) {
+          const u32x4 q = *reinterpret_cast<const u32x4*>(w_r + kk * E + e0 + ec);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) { v[2 * i] = q[i] & 0xffff; v[2 * i + 1] = q[i] >> 16; }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            v[i] = (kk < d && e0 + ec + i < E) ? w_r[kk * E + e0 + ec + i] : 0;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sm.wt[ec + i][row] = v[i];
+      }
+      __syncthreads();
+      // wave w: k range [k0 + 64w, k0 + 64w + 64) as two 32-deep MFMA steps
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int kl = wave * 64 + s * 32;
+        const int64_t kb = k0 + kl + 8 * (lane >> 4);
+        bf16x8 a;
+        if (tok_ok && vec_x && k0 + kl + 32 <= d) {
+          a = *reinterpret_cast<const bf16x8*>(xrow + kb);
+        } else {
+          uint16_t v[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] = (tok_ok && kb + i < d) ? xrow[kb + i] : 0;
+          a = pack_bf16x8(v);
+        }
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf) {
+          if (e0 + nf * 16 < E) {
+            const bf16x8 b = *reinterpret_cast<const bf16x8*>(&sm.wt[nf * 16 + (lane & 15)][kl + 8 * (lane >> 4)]);
+            acc[nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[nf], 0, 0, 0);
+          }
+        }
+      }
+    }
+    // C layout of the 16x16 MFMA: lane holds rows 4*(lane/16)+v, column lane%16
+#pragma unroll
+    for (int nf = 0; nf < 4; ++nf)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sm.red[wave][4 * (lane >> 4) + v][nf * 16 + (lane & 15)] = acc[nf][v];
+    __syncthreads();
+    for (int i = tid; i < RT_TOK * RT_EB; i += 256) {
+      const int t = i / RT_EB, e = e0 + i % RT_EB;
+      if (e < E) {
+        float z = ((sm.red[0][t][i % RT_EB] + sm.red[1][t][i % RT_EB]) + sm.red[2][t][i % RT_EB]) +
+                  sm.red[3][t][i % RT_EB];
+        if (bias) z += bias[e];
+        sm.z[t * E + e] = z;
+        if (tok0 + t < T) logits[(tok0 + t) * E + e] = z;
+      }
+    }
+  }
+  __syncthreads();
+  finish_tokens(sm, tok0, T, E, k, topk_idx, topk_w);
+}
+
+__global__ __launch_bounds__(256) void route_f32_kernel(
+    const float* __restrict__ x, const float* __restrict__ w_r, const float* __restrict__ bias,
+    int64_t T, int64_t d, int E, int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    float* __restrict__ logits) {
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  RouteSmem sm(smem_raw, E, false);
+  const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * RT_TOK;
+  for (int i = threadIdx.x; i < RT_TOK * E; i += 256) {
+    const int t = i / E, e = i % E;
+    const int64_t tok = tok0 + t;
+    float z = 0.f;
+    if (tok < T) {
+      const float* xr = x + tok * d;
+      for (int64_t c = 0; c < d; ++c) z = fmaf(xr[c], w_r[c * E + e], z);
+      if (bias) z += bias[e];
+      logits[tok * E + e] = z;
+    }
+    sm.z[t * E + e] = z;
+  }
+  __syncthreads();
+  finish_tokens(sm, tok0, T, E, k, topk_idx, topk_w);
+}
+
+}  // namespace
+
+moe_status_t launch_route(const void* x, const void* w_r, const float* bias, int dt, int64_t T,
+                          int64_t d, int E, int k, int32_t* topk_idx, float* topk_w, float* logits,
+                          hipStream_t s) {
+  if (T == 0) return MOE_OK;
+  const unsigned grid = static_cast<unsigned>((T + RT_TOK - 1) / RT_TOK);
+  const size_t smem = route_smem_bytes(E, dt == MOE_BF16);
+  if (dt == MOE_BF16) {
+    set_max_dynamic_smem(reinterpret_cast<const void*>(route_bf16_kernel), smem);
+    route_bf16_kernel<<<grid, 256, smem, s>>>(static_cast<const uint16_t*>(x),
+                                              static_cast<const uint16_t*>(w_r), bias, T, d, E, k,
+                                              topk_idx, topk_w, logits);
+  } else {
+    set_max_dynamic_smem(reinterpret_cast<const void*>(route_f32_kernel), smem);
+    route_f32_kernel<<<grid, 256, smem, s>>>(static_cast<const float*>(x),
+                                             static_cast<const float*>(w_r), bias, T, d, E, k,
+                                             topk_idx, topk_w, logits);
+  }
+  return check_launch("route kernel");
+}
+
+}  // namespace moe

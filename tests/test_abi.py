@@ -1,0 +1,130 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared entry point,
+and rejects bad arguments before touching a GPU (runs without one)."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+from sparse_mixture_experts_27_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.lib_path()):
+        pytest.skip("libmoe.so not built")
+    return B.lib()
+
+
+def test_header_declares_the_five_calls():
+    names = _declared()
+    for n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_layer_forward"):
+        assert n in names
+    assert set(names) == set(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", B.lib_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\s[TW]\s(moe_[a-z_]+)$", out, flags=re.M))
+    for n in _declared():
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+
+
+def test_status_strings(lib):
+    for s, name in B.STATUS.items():
+        assert lib.moe_status_string(s).decode().startswith(name)
+    assert b"unknown" in lib.moe_status_string(99)
+
+
+def _route(lib, **kw):
+    a = dict(x=16, w_r=16, bias=None, dt=B.MOE_BF16, T=4, d=64, E=8, k=2, idx=16, w=16, logits=16)
+    a.update(kw)
+    return lib.moe_route(a["x"], a["w_r"], a["bias"], a["dt"], a["T"], a["d"], a["E"], a["k"],
+                         a["idx"], a["w"], a["logits"], None)
+
+
+def test_route_validation(lib):
+    assert _route(lib, k=0) == 1
+    assert _route(lib, k=9) == 1
+    assert b"k=9" in lib.moe_last_error()
+    assert _route(lib, E=0) == 1
+    assert _route(lib, E=1025) == 1
+    assert _route(lib, dt=7) == 1
+    assert _route(lib, d=0) == 1
+    assert _route(lib, T=-1) == 1
+    assert _route(lib, x=None) == 1
+    assert _route(lib, logits=None) == 1
+    assert _route(lib, x=24) == 1            # misaligned
+    assert _route(lib, T=0) == 0             # no-op, nothing launched
+    assert lib.moe_last_error() == b""
+
+
+def test_dispatch_validation(lib):
+    need = lib.moe_dispatch_workspace_bytes(1000, 16)
+    assert need >= 2 * 4 * 16 * 4
+    assert lib.moe_dispatch_workspace_bytes(1000, 16) == need       # pure
+    args = [16, 1000, 16, 2, 0, 16, 16, 16, 16, 16, 16, need, None]
+    bad_k = list(args); bad_k[3] = 17
+    assert lib.moe_dispatch(*bad_k) == 1
+    bad_ws = list(args); bad_ws[11] = need - 1
+    assert lib.moe_dispatch(*bad_ws) == 3
+    nul = list(args); nul[5] = None
+    assert lib.moe_dispatch(*nul) == 1
+
+
+def test_ffn_validation(lib):
+    need = lib.moe_expert_ffn_workspace_bytes(8192, 64, 4096, 14336, B.MOE_ACT_SWIGLU, B.MOE_BF16)
+    assert need >= 8192 * 14336 * 2                     # holds the bf16 hidden activation
+    base = [16, 16, 2, 16, 64, 8192, 4096, 14336, B.MOE_ACT_SWIGLU, B.MOE_BF16, 16, 16, 16, 16, 16, need, None]
+    odd = list(base); odd[6] = 4000                    # d % 64 != 0 for bf16
+    assert lib.moe_expert_ffn(*odd) == 2
+    no_up = list(base); no_up[11] = None
+    assert lib.moe_expert_ffn(*no_up) == 1
+    small = list(base); small[15] = need - 1
+    assert lib.moe_expert_ffn(*small) == 3
+    bad_act = list(base); bad_act[8] = 5
+    assert lib.moe_expert_ffn(*bad_act) == 1
+
+
+def test_combine_validation(lib):
+    assert lib.moe_combine(16, 10, 16, 16, None, 4, 64, 2, 3, 16, None) == 1      # bad dtype
+    assert lib.moe_combine(16, 10, None, 16, None, 4, 64, 2, B.MOE_F32, 16, None) == 1
+    assert lib.moe_combine(None, 0, None, None, None, 0, 64, 2, B.MOE_F32, None, None) == 0
+
+
+def test_layer_validation_and_workspace(lib):
+    a = B.LayerArgs()
+    a.dt, a.act, a.T, a.d, a.F, a.E, a.k = B.MOE_BF16, B.MOE_ACT_SWIGLU, 4096, 4096, 14336, 64, 2
+    for f in ("x", "w_r", "w_gate", "w_up", "w_down", "out"):
+        setattr(a, f, 256)
+    need = lib.moe_layer_workspace_bytes(C.byref(a))
+    assert need > 4096 * 2 * 14336 * 2              # H for every routed row
+    a.ws, a.ws_bytes = 256, need - 1
+    assert lib.moe_layer_forward(C.byref(a), None) == 3
+    a.ws_bytes = need
+    a.w_up = None
+    assert lib.moe_layer_forward(C.byref(a), None) == 1
+    a.w_up = 256
+    a.s_gate = 256                                  # shared expert without s_down
+    assert lib.moe_layer_forward(C.byref(a), None) == 1
+    a.s_gate = None
+    a.d = 4000
+    assert lib.moe_layer_forward(C.byref(a), None) == 2
+    a.d = 4096
+    a.T = 0
+    assert lib.moe_layer_forward(C.byref(a), None) == 0
+    with_shared = B.LayerArgs.from_buffer_copy(a)
+    with_shared.T = 4096
+    with_shared.s_gate = with_shared.s_up = with_shared.s_down = 256
+    assert lib.moe_layer_workspace_bytes(C.byref(with_shared)) > need

@@ -1,0 +1,219 @@
+"""GPU parity: the HIP layer (through the C ABI) against the CPU oracle.
+
+Small cases run the oracle on every token; the five full-size workloads check routing
+and dispatch on every token and the expert FFN + combine on sampled tokens.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from sparse_mixture_experts_27_amd import binding as B
+from sparse_mixture_experts_27_amd import synth
+from sparse_mixture_experts_27_amd.configs import CONFIGS, MoEConfig
+from tests.gpu_helpers import (check_dispatch, check_output, check_route, expert_fetcher, layer_for,
+                               run_layer, say, shared_weights)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+# Cases the oracle finishes in seconds; each spans several tiles and ragged tails.
+SMALL = {
+    "tiny-gelu-f32": CONFIGS[1],
+    "f32-swiglu-ragged": MoEConfig("f32-swiglu", 11, T=203, d=96, E=5, k=2, F=160, act="swiglu", dtype="f32"),
+    "f32-shared-capacity": MoEConfig("f32-sc", 12, T=150, d=64, E=6, k=2, F=128, act="swiglu", dtype="f32",
+                                     shared=True, capacity=40, bias_var=0.5),
+    "bf16-swiglu-multitile": MoEConfig("bf16-mt", 13, T=700, d=512, E=4, k=2, F=640, act="swiglu", dtype="bf16"),
+    "bf16-gelu": MoEConfig("bf16-gelu", 14, T=300, d=256, E=8, k=2, F=512, act="gelu", dtype="bf16"),
+    "bf16-shared-bias": MoEConfig("bf16-shared", 15, T=513, d=256, E=6, k=2, F=384, act="swiglu",
+                                  dtype="bf16", shared=True, bias_var=0.5),
+    "bf16-capacity": MoEConfig("bf16-cap", 16, T=400, d=256, E=8, k=2, F=256, act="swiglu", dtype="bf16",
+                               capacity=60, bias_var=1.0),
+    "bf16-decode": MoEConfig("bf16-dec", 17, T=5, d=512, E=64, k=2, F=1024, act="swiglu", dtype="bf16"),
+    "bf16-k1": MoEConfig("bf16-k1", 18, T=257, d=128, E=8, k=1, F=192, act="swiglu", dtype="bf16"),
+    "bf16-k-eq-E": MoEConfig("bf16-kE", 19, T=130, d=128, E=4, k=4, F=128, act="swiglu", dtype="bf16"),
+    "bf16-single-expert": MoEConfig("bf16-E1", 20, T=333, d=128, E=1, k=1, F=256, act="gelu", dtype="bf16"),
+    "bf16-e128-top2": MoEConfig("bf16-e128", 21, T=200, d=128, E=128, k=2, F=128, act="swiglu", dtype="bf16"),
+    "bf16-e384-top6-shared": MoEConfig("bf16-e384", 22, T=96, d=128, E=384, k=6, F=64, act="swiglu",
+                                       dtype="bf16", shared=True),
+    "bf16-capacity-one": MoEConfig("bf16-c1", 23, T=64, d=128, E=4, k=2, F=64, act="swiglu", dtype="bf16",
+                                   capacity=1),
+}
+
+
+def _x64(inp):
+    return synth.to_numpy(inp["x"]), synth.to_numpy(inp["w_r"]), synth.to_numpy(inp["bias"])
+
+
+def _run_and_check(cfg, inp, tokens=None, out_dtype=torch.float32):
+    say(f"[case] {cfg.label} out={out_dtype}")
+    res = run_layer(cfg, inp, out_dtype)
+    x64, wr64, b64 = _x64(inp)
+    report = {}
+    z_o, flip = check_route(cfg, x64, wr64, b64, res, report)
+    check_dispatch(cfg, res)
+    check_output(cfg, x64, z_o, res, expert_fetcher(cfg, inp), shared_weights(inp), tokens, report,
+                 out_bf16=out_dtype == torch.bfloat16)
+    report["n_dropped"] = res["n_dropped"]
+    say(f"[ok] {cfg.name}: {report}")
+    return res, report
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_small(name):
+    cfg = SMALL[name]
+    inp = synth.make_inputs(cfg, DEV)
+    _run_and_check(cfg, inp)
+
+
+@pytest.mark.parametrize("name", ["bf16-shared-bias", "bf16-capacity", "bf16-e384-top6-shared"])
+def test_layer_small_bf16_output(name):
+    """The same layers writing a bf16 output (rounded once from the fp32 accumulator)."""
+    cfg = SMALL[name]
+    inp = synth.make_inputs(cfg, DEV)
+    _run_and_check(cfg, inp, out_dtype=torch.bfloat16)
+
+
+def test_skewed_one_expert_takes_all():
+    """A huge offset on one expert sends every token there: one group of T rows, spanning
+    several M-tiles with a ragged tail; the other groups are empty."""
+    cfg = MoEConfig("skew", 24, T=600, d=128, E=6, k=2, F=128, act="swiglu", dtype="bf16", bias_var=0.0)
+    inp = synth.make_inputs(cfg, DEV)
+    inp["bias"] = torch.tensor([0, 0, 0, 50.0, 0, 0], device=DEV)
+    res, _ = _run_and_check(cfg, inp)
+    assert res["counts"][3] == cfg.T
+
+
+def test_all_dropped_tokens_are_zero():
+    cfg = MoEConfig("drop", 25, T=200, d=128, E=4, k=2, F=64, act="swiglu", dtype="bf16", capacity=3)
+    inp = synth.make_inputs(cfg, DEV)
+    res, rep = _run_and_check(cfg, inp)
+    dead = np.all(res["inv"] < 0, axis=1)
+    assert dead.any() and np.all(res["out"][dead] == 0.0)
+    assert rep["n_dropped"] == cfg.T * cfg.k - 3 * cfg.E
+
+
+def test_worked_example_on_gpu():
+    """The page's worked mixture through the whole GPU layer (fp32): logits ln 3 and 0
+    on E1 and E3, experts built to return the page's two vectors."""
+    import json
+    import math
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_combine.json")))
+    d, E, F = 3, 4, 1
+    x = torch.zeros((1, d), device=DEV)
+    x[0, 0] = 1.0
+    w_r = torch.zeros((d, E), device=DEV)
+    w_r[0] = torch.tensor([math.log(3.0), -10.0, 0.0, -10.0])
+    targets = torch.tensor([g["expert_outputs"][0], [9.0] * 3, g["expert_outputs"][1], [-9.0] * 3], device=DEV)
+    wg = torch.zeros((E, F, d), device=DEV)
+    wg[:, 0, 0] = 1.0
+    wu = wg.clone()
+    hval = 1.0 / (1.0 + math.exp(-1.0))
+    wd = (targets / hval)[:, :, None].contiguous()
+    L = B.Layer(w_r, wg, wu, wd, 2, act="swiglu")
+    out = L(x)
+    torch.cuda.synchronize()
+    assert L.topk_idx.cpu().tolist()[0] == g["chosen"]
+    np.testing.assert_allclose(L.topk_w.cpu().numpy()[0], g["weights"], atol=1e-6)
+    np.testing.assert_allclose(out.cpu().numpy()[0], g["mixture"], atol=1e-5)
+
+
+def test_stage_entry_points():
+    """The four stage calls used one by one, each against the oracle."""
+    cfg = MoEConfig("stages", 26, T=300, d=256, E=8, k=2, F=320, act="swiglu", dtype="bf16",
+                    shared=True, capacity=70, bias_var=0.5)
+    inp = synth.make_inputs(cfg, DEV)
+    idx, w, logits = B.route(inp["x"], inp["w_r"], cfg.k, bias=inp["bias"])
+    x64, wr64, b64 = _x64(inp)
+    res = dict(idx=idx.cpu().numpy().astype(np.int64), w=w.cpu().numpy().astype(np.float64),
+               logits=logits.cpu().numpy())
+    rep = {}
+    z_o, _ = check_route(cfg, x64, wr64, b64, res, rep)
+    dp = B.dispatch(idx, cfg.E, cfg.capacity)
+    torch.cuda.synchronize()
+    res.update(counts=dp.counts.cpu().numpy().astype(np.int64), offsets=dp.offsets.cpu().numpy().astype(np.int64),
+               perm=dp.perm.cpu().numpy().astype(np.int64), inv=dp.inv.cpu().numpy().astype(np.int64),
+               n_dropped=int(dp.n_dropped.item()))
+    odp = check_dispatch(cfg, res)
+    R = int(odp["offsets"][-1])
+    y = B.expert_ffn(inp["x"], dp.offsets, inp["w_gate"], inp["w_up"], inp["w_down"], cfg.T * cfg.k,
+                     perm=dp.perm, k=cfg.k, act=cfg.act)
+    # routed rows against the oracle's per-expert FFN
+    fetch = expert_fetcher(cfg, inp)
+    y_ref = np.zeros((R, cfg.d))
+    for e in range(cfg.E):
+        rows = np.arange(odp["offsets"][e], odp["offsets"][e + 1])
+        if rows.size:
+            y_ref[rows] = O.expert_ffn(x64[odp["perm"][rows] // cfg.k], cfg.act, *fetch(e))
+    yg = y[:R].cpu().numpy().astype(np.float64)
+    rms = np.sqrt(np.mean(y_ref ** 2))
+    assert np.abs(yg - y_ref).max() <= 2e-2 * rms
+    # shared expert through the same call: identity rows, one group
+    sh_off = torch.tensor([0, cfg.T], dtype=torch.int32, device=DEV)
+    ys = B.expert_ffn(inp["x"], sh_off, inp["s_gate"][None], inp["s_up"][None], inp["s_down"][None], cfg.T,
+                      act=cfg.act)
+    ys_ref = O.expert_ffn(x64, cfg.act, *shared_weights(inp))
+    assert np.abs(ys.cpu().numpy() - ys_ref).max() <= 2e-2 * np.sqrt(np.mean(ys_ref ** 2))
+    # combine with the shared output
+    out = B.combine(y, dp.inv, w, torch.float32, shared=ys)
+    torch.cuda.synchronize()
+    keep = res["inv"] >= 0
+    ref = O.routed_output(x64, res["idx"], O.topk_weights(z_o, res["idx"]), keep, cfg.act, fetch,
+                          shared_weights(inp))
+    got = out.float().cpu().numpy()
+    assert np.abs(got - ref).max() <= 2e-2 * np.sqrt(np.mean(ref ** 2))
+
+
+def test_deterministic_bits():
+    cfg = SMALL["bf16-shared-bias"]
+    inp = synth.make_inputs(cfg, DEV)
+    L = layer_for(cfg, inp)
+    a = L(inp["x"]).clone()
+    i1, p1 = L.topk_idx.clone(), L.perm.clone()
+    b = L(inp["x"]).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert torch.equal(i1, L.topk_idx) and torch.equal(p1, L.perm)
+
+
+def test_empty_batch_is_noop():
+    cfg = SMALL["bf16-gelu"].scaled(T=0)
+    inp = synth.make_inputs(SMALL["bf16-gelu"], DEV)
+    L = layer_for(cfg, inp)
+    out = L(inp["x"][:0])
+    torch.cuda.synchronize()
+    assert out.shape == (0, cfg.d)
+
+
+# ---- the five workloads at full size (routing on every token, outputs sampled) ----
+SAMPLES = {1: None, 2: 8, 3: 10, 4: 12, 5: None}
+
+
+@pytest.mark.parametrize("num", [2, 3, 4, 5])
+def test_workload_full_size(num):
+    cfg = CONFIGS[num]
+    say(f"[case] full size {cfg.label}: generating inputs")
+    inp = synth.make_inputs(cfg, DEV)
+    torch.cuda.synchronize()
+    res = run_layer(cfg, inp)
+    x64, wr64, b64 = _x64(inp)
+    rep = {}
+    z_o, flip = check_route(cfg, x64, wr64, b64, res, rep)
+    check_dispatch(cfg, res)
+    assert res["counts"].sum() == cfg.T * cfg.k
+    n = SAMPLES[num]
+    tokens = None
+    if n is not None:
+        rng = np.random.default_rng(num)
+        tokens = np.sort(rng.choice(np.nonzero(~flip)[0], size=n, replace=False))
+    check_output(cfg, x64, z_o, res, expert_fetcher(cfg, inp), shared_weights(inp), tokens, rep)
+    rep["n_dropped"] = res["n_dropped"]
+    rep["drop_rate"] = res["n_dropped"] / (cfg.T * cfg.k)
+    rep["load_min_max"] = (int(res["counts"].min()), int(res["counts"].max()))
+    say(f"[ok] {cfg.name}: {rep}")
+    del inp
+    torch.cuda.empty_cache()
