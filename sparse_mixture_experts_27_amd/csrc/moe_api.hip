@@ -170,7 +170,7 @@ static size_t layer_layout(const moe_layer_args_t* a, bool carve, WsCarver& c, i
   const int64_t T = a->T;
   const bool shared = a->s_gate != nullptr;
   const int64_t max_rows = T * a->k + (shared ? T : 0);
-  *plan = ffn_plan(max_rows, a->E, shared, a->d, a->F, a->act, a->dt);
+  *plan = ffn_plan(max_rows, a->E, shared, a->d, a->F, a->act, a->dt, a->capacity);
   float* lg = c.take<float>(static_cast<size_t>(T) * a->E);
   int32_t* ix = c.take<int32_t>(static_cast<size_t>(T) * a->k);
   float* tw = c.take<float>(static_cast<size_t>(T) * a->k);

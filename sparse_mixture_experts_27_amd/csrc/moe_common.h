@@ -70,11 +70,15 @@ struct FfnProblem {
 };
 
 struct FfnPlan {
+  int bm;                   // rows per M-tile
+  int nw;                   // waves per workgroup of the bf16 GEMMs (4 or 8)
   int splits;               // split-K factor of the down projection
   int64_t max_mtiles;
   size_t ws_bytes;
 };
-FfnPlan ffn_plan(int64_t max_rows, int G, bool has_shared, int64_t d, int64_t F, int act, int dt);
+// capacity: per-group row limit if known (0 = unknown); only tunes the tile height.
+FfnPlan ffn_plan(int64_t max_rows, int G, bool has_shared, int64_t d, int64_t F, int act, int dt,
+                 int64_t capacity = 0);
 // y: [splits][max_rows][d] fp32 partial sums when plan.splits > 1 and reduce_splits is
 // false; otherwise [max_rows][d] final.
 // ev (nullable): events recorded after the schedule, up-projection and down-projection.

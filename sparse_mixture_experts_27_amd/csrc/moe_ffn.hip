@@ -20,6 +20,8 @@
 // tiles: the tiles of one expert share its activation rows in that XCD's L2.
 #include "moe_common.h"
 
+#include <cstdlib>
+
 namespace moe {
 namespace {
 
@@ -161,14 +163,30 @@ __device__ __forceinline__ int64_t a_source_row(const GemmArgs& p, int mode, int
   return p.perm ? static_cast<int64_t>(p.perm[r] / p.k_div) : r;
 }
 
-template <int MODE>
-__global__ __launch_bounds__(256, 1) void ffn_gemm_bf16_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * BK];   // 2 x 32 KB
+// Tile: MT*16 rows x 256 MFMA columns, K advanced BK=64 per pipeline stage, NW waves of
+// NF 16-column fragments each (NW * NF * 16 = 256).  With NW = 8 two waves share each
+// SIMD, so one wave's memory and LDS latency hides behind the other's MFMAs.
+// Weights: a ring of 3 register slots per wave (stage s is multiplied while s+1 and s+2
+// are in flight).  Activations: loaded one stage ahead into registers and stored into
+// a ring of 3 LDS slots.  Every global load is unconditional (padding rows read a valid
+// row of the tile and inactive waves read valid weight rows; neither result is stored)
+// so the compiler's memory counters stay exact, and activation loads are issued before
+// weight loads so that waiting for one stage's activations never waits for weights.
+// Per-lane addresses are 32-bit byte offsets from uniform base pointers.
+template <int MODE, int MT, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void ffn_gemm_bf16_kernel(GemmArgs p) {
+  constexpr int NT = NW * 64;                     // threads
+  constexpr int NF = 256 / (16 * NW);             // 16-column fragments per wave
+  constexpr int WCOLS = NF * 16;                  // MFMA columns per wave
+  constexpr int BMT = MT * 16;
+  constexpr int AR = (BMT * 8 + NT - 1) / NT;     // 16-byte activation chunks per thread per stage
+  constexpr int RING = 3;
+  static_assert(NF >= 2 && NF * 16 * NW == 256, "tile shape");
+  __shared__ __attribute__((aligned(16))) uint16_t As[RING][BMT * BK];
   TileInfo ti;
-  if (!decode_tile(p, BM, ti)) return;
+  if (!decode_tile(p, BMT, ti)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nrows16 = (ti.nrows + 15) & ~15;
-  const int nmf = nrows16 >> 4;
+  const int nmf = (ti.nrows + 15) >> 4;
 
   // ---- K range of this tile
   int64_t k_begin = 0, k_end = p.K;
@@ -176,93 +194,93 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_bf16_kernel(GemmArgs p) {
     k_begin = static_cast<int64_t>(ti.split) * p.k_chunk;
     k_end = k_begin + p.k_chunk < p.K ? k_begin + p.k_chunk : p.K;
   }
-  const int nst = static_cast<int>((k_end - k_begin) / BK);
+  const int nst = k_end > k_begin ? static_cast<int>((k_end - k_begin) / BK) : 0;
 
-  // ---- weight rows (columns of C) owned by this wave
+  // ---- weight rows (columns of C) owned by this wave.  SwiGLU: the first half of the
+  // fragments are gate rows, the second half the up rows of the same hidden units.
   const bool shared_grp = ti.g >= p.G;
-  const uint16_t* W0 = static_cast<const uint16_t*>(shared_grp ? p.sw0 : p.w0);
-  const uint16_t* W1 = static_cast<const uint16_t*>(shared_grp ? p.sw1 : p.w1);
   const int64_t wstride = shared_grp ? 0 : static_cast<int64_t>(ti.g) * p.N * p.K;
+  const char* Wb0 = reinterpret_cast<const char*>(static_cast<const uint16_t*>(shared_grp ? p.sw0 : p.w0) + wstride);
+  const char* Wb1 = reinterpret_cast<const char*>(static_cast<const uint16_t*>(shared_grp ? p.sw1 : p.w1) + wstride);
+  if (MODE != MODE_SWIGLU_UP) Wb1 = Wb0;
   int64_t col_base;                         // first output column of this wave
-  if (MODE == MODE_SWIGLU_UP) col_base = static_cast<int64_t>(ti.ntile) * 128 + wave * 32;
-  else col_base = static_cast<int64_t>(ti.ntile) * 256 + wave * 64;
+  if (MODE == MODE_SWIGLU_UP) col_base = static_cast<int64_t>(ti.ntile) * 128 + wave * (WCOLS / 2);
+  else col_base = static_cast<int64_t>(ti.ntile) * 256 + wave * WCOLS;
   const bool wave_on = col_base < p.N;
-  const uint16_t* bptr[4];
+  uint32_t boff[NF];                        // byte offsets of this lane's weight rows
 #pragma unroll
-  for (int nf = 0; nf < 4; ++nf) {
-    int64_t wrow;
-    const uint16_t* Wm;
-    if (MODE == MODE_SWIGLU_UP) {
-      wrow = col_base + (nf & 1) * 16 + (lane & 15);
-      Wm = (nf < 2) ? W0 : W1;
-    } else {
-      wrow = col_base + nf * 16 + (lane & 15);
-      Wm = W0;
-    }
-    if (!wave_on) wrow = 0;
-    bptr[nf] = Wm + wstride + wrow * p.K + k_begin + 8 * (lane >> 4);
+  for (int nf = 0; nf < NF; ++nf) {
+    int64_t wrow = (MODE == MODE_SWIGLU_UP) ? col_base + (nf % (NF / 2)) * 16 + (lane & 15)
+                                            : col_base + nf * 16 + (lane & 15);
+    if (!wave_on) wrow = lane & 15;         // a valid row; the result is not stored
+    boff[nf] = static_cast<uint32_t>((wrow * p.K + k_begin + 8 * (lane >> 4)) * 2);
   }
 
-  // ---- activation rows loaded by this thread: rows i*32 + tid/8, 16-byte chunk tid%8
-  const int chunk = tid & 7;
-  int64_t arow[8];
+  // ---- activation chunks loaded by this thread: chunk q = i*NT + tid -> row q/8 (mod
+  // the tile height; a repeated row writes identical bytes), 16-byte column q%8
+  const char* Ab = reinterpret_cast<const char*>(p.a);
+  uint32_t aoff[AR];
+  int arow_l[AR], achunk[AR];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = i * 32 + (tid >> 3);
-    arow[i] = (r < ti.nrows) ? a_source_row(p, MODE, ti.g, ti.row_begin + r) : -1;
+  for (int i = 0; i < AR; ++i) {
+    const int q = i * NT + tid;
+    const int r = (q >> 3) % BMT;
+    achunk[i] = q & 7;
+    arow_l[i] = r;
+    const int rr = r < ti.nrows ? r : 0;    // padding rows repeat row 0 of the tile
+    aoff[i] = static_cast<uint32_t>((a_source_row(p, MODE, ti.g, ti.row_begin + rr) * p.K + k_begin +
+                                     achunk[i] * 8) * 2);
   }
-  const uint16_t* A = p.a;
 
-  u32x4 ra[8];
-  bf16x8 rb[2][2][4];      // [buffer][k32 step][fragment]
+  u32x4 ra[AR];
+  bf16x8 rb[RING][2][NF];                   // [ring slot][k32 step][fragment]
 
   auto load_a = [&](int st) {
-    const int64_t k0 = k_begin + static_cast<int64_t>(st) * BK + chunk * 8;
+    st = st < nst ? st : nst - 1;
+    const uint32_t ko = static_cast<uint32_t>(st) * (BK * 2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (i * 32 < nrows16) {
-        if (arow[i] >= 0) ra[i] = *reinterpret_cast<const u32x4*>(A + arow[i] * p.K + k0);
-        else ra[i] = u32x4{0u, 0u, 0u, 0u};
-      }
+    for (int i = 0; i < AR; ++i) ra[i] = *reinterpret_cast<const u32x4*>(Ab + (aoff[i] + ko));
+  };
+  auto store_a = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < AR; ++i) {
+      const int r = arow_l[i];
+      *reinterpret_cast<u32x4*>(&As[slot][r * BK + ((achunk[i] ^ (r & 7)) * 8)]) = ra[i];
     }
   };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = i * 32 + (tid >> 3);
-      if (i * 32 < nrows16 && r < nrows16)
-        *reinterpret_cast<u32x4*>(&As[buf][r * BK + ((chunk ^ (r & 7)) * 8)]) = ra[i];
-    }
-  };
-  auto load_b = [&](int st, int buf) {
-    if (!wave_on) return;
-    const int64_t ko = static_cast<int64_t>(st) * BK;
+  auto load_b = [&](int st, int slot) {
+    st = st < nst ? st : nst - 1;
+    const uint32_t ko = static_cast<uint32_t>(st) * (BK * 2);
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int nf = 0; nf < 4; ++nf)
-        rb[buf][s][nf] = *reinterpret_cast<const bf16x8*>(bptr[nf] + ko + s * 32);
+      for (int nf = 0; nf < NF; ++nf) {
+        const char* base = (MODE == MODE_SWIGLU_UP && nf >= NF / 2) ? Wb1 : Wb0;
+        rb[slot][s][nf] = *reinterpret_cast<const bf16x8*>(base + (boff[nf] + ko + s * 64));
+      }
+  };
+  auto read_a = [&](int slot, int s, int mf) {
+    const int r = mf * 16 + (lane & 15);
+    const int c = (s * 4 + (lane >> 4)) ^ (r & 7);
+    return *reinterpret_cast<const bf16x8*>(&As[slot][r * BK + c * 8]);
   };
 
-  f32x4 acc[16][4];
+  f32x4 acc[MT][NF];
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int abuf, int bbuf) {
-    if (!wave_on) return;
+  auto compute = [&](int aslot, int bslot) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
-      for (int mf = 0; mf < 16; ++mf) {
+      for (int mf = 0; mf < MT; ++mf) {
         if (mf < nmf) {
-          const int r = mf * 16 + (lane & 15);
-          const int c = (s * 4 + (lane >> 4)) ^ (r & 7);
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&As[abuf][r * BK + c * 8]);
+          const bf16x8 a = read_a(aslot, s, mf);
 #pragma unroll
-          for (int nf = 0; nf < 4; ++nf)
-            acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, rb[bbuf][s][nf], acc[mf][nf], 0, 0, 0);
+          for (int nf = 0; nf < NF; ++nf)
+            acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, rb[bslot][s][nf], acc[mf][nf], 0, 0, 0);
         }
       }
     }
@@ -271,28 +289,27 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_bf16_kernel(GemmArgs p) {
   if (nst > 0) {
     load_a(0);
     load_b(0, 0);
+    load_b(1, 1);
     store_a(0);
     __syncthreads();
-    for (int st = 0; st < nst; st += 2) {
-      // even stage: compute buffer 0 while stage st+1 is in flight
-      const bool more1 = st + 1 < nst;
-      if (more1) { load_a(st + 1); load_b(st + 1, 1); }
-      compute(0, 0);
-      if (more1) store_a(1);
-      __syncthreads();
-      if (!more1) break;
-      const bool more2 = st + 2 < nst;
-      if (more2) { load_a(st + 2); load_b(st + 2, 0); }
-      compute(1, 1);
-      if (more2) store_a(0);
-      __syncthreads();
+    for (int base = 0; base < nst; base += RING) {
+#pragma unroll
+      for (int ph = 0; ph < RING; ++ph) {
+        const int st = base + ph;
+        if (st >= nst) break;
+        load_a(st + 1);
+        load_b(st + 2, (ph + 2) % RING);
+        compute(ph, ph);
+        store_a((ph + 1) % RING);
+        __syncthreads();
+      }
     }
   }
 
   // ---- epilogue.  C layout: lane holds rows 4*(lane/16)+v of each 16x16 block, column lane%16.
   if (!wave_on) return;
 #pragma unroll
-  for (int mf = 0; mf < 16; ++mf) {
+  for (int mf = 0; mf < MT; ++mf) {
     if (mf < nmf) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
@@ -302,22 +319,22 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_bf16_kernel(GemmArgs p) {
           if (MODE == MODE_SWIGLU_UP) {
             uint16_t* H = static_cast<uint16_t*>(p.out);
 #pragma unroll
-            for (int nf = 0; nf < 2; ++nf) {
+            for (int nf = 0; nf < NF / 2; ++nf) {
               const int64_t f = col_base + nf * 16 + (lane & 15);
-              const float h = silu_f(acc[mf][nf][v]) * acc[mf][nf + 2][v];
+              const float h = silu_f(acc[mf][nf][v]) * acc[mf][nf + NF / 2][v];
               H[orow * p.N + f] = f32_to_bf16(h);
             }
           } else if (MODE == MODE_GELU_UP) {
             uint16_t* H = static_cast<uint16_t*>(p.out);
 #pragma unroll
-            for (int nf = 0; nf < 4; ++nf) {
+            for (int nf = 0; nf < NF; ++nf) {
               const int64_t f = col_base + nf * 16 + (lane & 15);
               H[orow * p.N + f] = f32_to_bf16(gelu_f(acc[mf][nf][v]));
             }
           } else {
             float* Y = static_cast<float*>(p.out) + static_cast<int64_t>(ti.split) * p.split_stride;
 #pragma unroll
-            for (int nf = 0; nf < 4; ++nf) {
+            for (int nf = 0; nf < NF; ++nf) {
               const int64_t n = col_base + nf * 16 + (lane & 15);
               Y[orow * p.N + n] = acc[mf][nf][v];
             }
@@ -415,18 +432,59 @@ __global__ __launch_bounds__(256) void ffn_reduce_splits_kernel(const float* __r
   }
 }
 
+// Launch one bf16 grouped GEMM with the M-tile (MT*16 rows) chosen by the plan.
+template <int MODE>
+void launch_bf16_gemm(int bm, int nw, int64_t grid, const GemmArgs& g, hipStream_t s) {
+  const unsigned gr = static_cast<unsigned>(grid);
+  if (nw == 8) {
+    switch (bm) {
+      case 32: ffn_gemm_bf16_kernel<MODE, 2, 8><<<gr, 512, 0, s>>>(g); break;
+      case 64: ffn_gemm_bf16_kernel<MODE, 4, 8><<<gr, 512, 0, s>>>(g); break;
+      case 128: ffn_gemm_bf16_kernel<MODE, 8, 8><<<gr, 512, 0, s>>>(g); break;
+      default: ffn_gemm_bf16_kernel<MODE, 16, 8><<<gr, 512, 0, s>>>(g); break;
+    }
+  } else {
+    switch (bm) {
+      case 32: ffn_gemm_bf16_kernel<MODE, 2, 4><<<gr, 256, 0, s>>>(g); break;
+      case 64: ffn_gemm_bf16_kernel<MODE, 4, 4><<<gr, 256, 0, s>>>(g); break;
+      case 128: ffn_gemm_bf16_kernel<MODE, 8, 4><<<gr, 256, 0, s>>>(g); break;
+      default: ffn_gemm_bf16_kernel<MODE, 16, 4><<<gr, 256, 0, s>>>(g); break;
+    }
+  }
+}
+
 }  // namespace
 
-FfnPlan ffn_plan(int64_t max_rows, int G, bool has_shared, int64_t d, int64_t F, int act, int dt) {
+// M-tile height: the smallest of 32/64/128/256 rows that holds a typical group in one
+// tile, so each expert's weights stream once.  The rows per group are only known on the
+// device; the host estimate is the capacity when one is set, else 1.6x the mean load
+// (plus a margin for small loads).
+FfnPlan ffn_plan(int64_t max_rows, int G, bool has_shared, int64_t d, int64_t F, int act, int dt,
+                 int64_t capacity) {
   FfnPlan pl{};
-  const int bm = dt == MOE_BF16 ? BM : BM_F32;
   (void)act;
   const int Gt = G + (has_shared ? 1 : 0);
-  pl.max_mtiles = (max_rows + bm - 1) / bm + Gt + 1;
+  if (dt == MOE_BF16) {
+    const int64_t routed = max_rows;
+    double est = 1.6 * static_cast<double>(routed) / (G > 0 ? G : 1) + 16.0;
+    if (capacity > 0 && static_cast<double>(capacity) < est) est = static_cast<double>(capacity);
+    pl.bm = est <= 32 ? 32 : est <= 64 ? 64 : est <= 128 ? 128 : BM;
+    if (has_shared) pl.bm = BM;
+    // tuning override of the tile height (32, 64, 128 or 256 rows)
+    if (const char* o = getenv("MOE_TILE_ROWS")) {
+      const int v = atoi(o);
+      if (v == 32 || v == 64 || v == 128 || v == 256) pl.bm = v;
+    }
+    pl.nw = 8;
+    if (const char* o = getenv("MOE_TILE_WAVES")) pl.nw = atoi(o) == 4 ? 4 : 8;
+  } else {
+    pl.bm = BM_F32;
+  }
+  pl.max_mtiles = (max_rows + pl.bm - 1) / pl.bm + Gt + 1;
   pl.splits = 1;
   if (dt == MOE_BF16) {
     const int64_t nt2 = (d + 255) / 256;
-    int64_t est = (max_rows + bm - 1) / bm;
+    int64_t est = (max_rows + pl.bm - 1) / pl.bm;
     const int64_t busy = G < max_rows ? G : max_rows;
     if (busy > est) est = busy;
     while (est * nt2 * pl.splits < 2048 && F / (BK * pl.splits * 2) >= 8) pl.splits *= 2;
@@ -447,7 +505,7 @@ moe_status_t launch_ffn(const FfnProblem& p, const FfnPlan& plan, float* y, bool
   const bool has_shared = p.shared_rows > 0;
   const int Gt = p.G + (has_shared ? 1 : 0);
   const bool bf = p.dt == MOE_BF16;
-  const int bm = bf ? BM : BM_F32;
+  const int bm = plan.bm;
   WsCarver c(ws);
   int32_t* sched = c.take<int32_t>(sched_words(Gt));
   void* H = bf ? static_cast<void*>(c.take<uint16_t>(static_cast<size_t>(p.max_rows) * p.F))
@@ -487,8 +545,8 @@ moe_status_t launch_ffn(const FfnProblem& p, const FfnPlan& plan, float* y, bool
   if (bf) {
     g.nt = static_cast<int>(swiglu ? (p.F + 127) / 128 : (p.F + 255) / 256);
     const int64_t grid = ((plan.max_mtiles * g.nt + 7) / 8) * 8;
-    if (swiglu) ffn_gemm_bf16_kernel<MODE_SWIGLU_UP><<<static_cast<unsigned>(grid), 256, 0, s>>>(g);
-    else ffn_gemm_bf16_kernel<MODE_GELU_UP><<<static_cast<unsigned>(grid), 256, 0, s>>>(g);
+    if (swiglu) launch_bf16_gemm<MODE_SWIGLU_UP>(bm, plan.nw, grid, g, s);
+    else launch_bf16_gemm<MODE_GELU_UP>(bm, plan.nw, grid, g, s);
   } else {
     g.nt = static_cast<int>((p.F + 63) / 64);
     const int64_t grid = ((plan.max_mtiles * g.nt + 7) / 8) * 8;
@@ -514,7 +572,7 @@ moe_status_t launch_ffn(const FfnProblem& p, const FfnPlan& plan, float* y, bool
     g.split_stride = p.max_rows * p.d;
     g.out = plan.splits > 1 && reduce_splits ? static_cast<void*>(part) : static_cast<void*>(y);
     const int64_t grid = ((plan.max_mtiles * g.nt * g.splits + 7) / 8) * 8;
-    ffn_gemm_bf16_kernel<MODE_DOWN><<<static_cast<unsigned>(grid), 256, 0, s>>>(g);
+    launch_bf16_gemm<MODE_DOWN>(bm, plan.nw, grid, g, s);
   } else {
     g.nt = static_cast<int>((p.d + 63) / 64);
     g.k_chunk = p.F;
