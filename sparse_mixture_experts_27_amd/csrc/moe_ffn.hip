@@ -217,39 +217,45 @@ __global__ __launch_bounds__(NW * 64, 1) void ffn_gemm_bf16_kernel(GemmArgs p) {
   }
 
   // ---- activation chunks loaded by this thread: chunk q = i*NT + tid -> row q/8 (mod
-  // the tile height; a repeated row writes identical bytes), 16-byte column q%8
+  // the tile height; a repeated row writes identical bytes), 16-byte column q%8 = tid%8.
+  // The XOR swizzle uses row%8 = (tid/8)%8 for every i (NT/8 is a multiple of 8).
   const char* Ab = reinterpret_cast<const char*>(p.a);
+  constexpr bool WRAP = (AR * NT / 8) > BMT;
+  const int chunk = tid & 7;
   uint32_t aoff[AR];
-  int arow_l[AR], achunk[AR];
 #pragma unroll
   for (int i = 0; i < AR; ++i) {
-    const int q = i * NT + tid;
-    const int r = (q >> 3) % BMT;
-    achunk[i] = q & 7;
-    arow_l[i] = r;
+    const int r = WRAP ? ((i * NT + tid) >> 3) % BMT : (i * NT + tid) >> 3;
     const int rr = r < ti.nrows ? r : 0;    // padding rows repeat row 0 of the tile
     aoff[i] = static_cast<uint32_t>((a_source_row(p, MODE, ti.g, ti.row_begin + rr) * p.K + k_begin +
-                                     achunk[i] * 8) * 2);
+                                     chunk * 8) * 2);
   }
+  const int st_row0 = WRAP ? (tid >> 3) % BMT : (tid >> 3);
+  const int st_off0 = st_row0 * BK + ((chunk ^ (st_row0 & 7)) * 8);   // element offset in a slot
 
-  u32x4 ra[AR];
-  bf16x8 rb[RING][2][NF];                   // [ring slot][k32 step][fragment]
+  u32x4 ra[2][AR];                          // activation register ring: 2 stages
+  bf16x8 rb[RING][2][NF];                   // weight register ring: [slot][k32 step][fragment]
 
-  auto load_a = [&](int st) {
-    st = st < nst ? st : nst - 1;
+  auto clamp_stage = [&](int st) { return st < 0 ? 0 : (st < nst ? st : nst - 1); };
+  auto load_a = [&](int st, int aslot) {
+    st = clamp_stage(st);
     const uint32_t ko = static_cast<uint32_t>(st) * (BK * 2);
 #pragma unroll
-    for (int i = 0; i < AR; ++i) ra[i] = *reinterpret_cast<const u32x4*>(Ab + (aoff[i] + ko));
+    for (int i = 0; i < AR; ++i) ra[aslot][i] = *reinterpret_cast<const u32x4*>(Ab + (aoff[i] + ko));
   };
-  auto store_a = [&](int slot) {
+  auto store_a = [&](int aslot, int lslot) {
 #pragma unroll
     for (int i = 0; i < AR; ++i) {
-      const int r = arow_l[i];
-      *reinterpret_cast<u32x4*>(&As[slot][r * BK + ((achunk[i] ^ (r & 7)) * 8)]) = ra[i];
+      if (WRAP) {
+        const int r = ((i * NT + tid) >> 3) % BMT;
+        *reinterpret_cast<u32x4*>(&As[lslot][r * BK + ((chunk ^ (r & 7)) * 8)]) = ra[aslot][i];
+      } else {
+        *reinterpret_cast<u32x4*>(&As[lslot][st_off0 + i * (NT / 8) * BK]) = ra[aslot][i];
+      }
     }
   };
   auto load_b = [&](int st, int slot) {
-    st = st < nst ? st : nst - 1;
+    st = clamp_stage(st);
     const uint32_t ko = static_cast<uint32_t>(st) * (BK * 2);
 #pragma unroll
     for (int s = 0; s < 2; ++s)
@@ -258,6 +264,14 @@ __global__ __launch_bounds__(NW * 64, 1) void ffn_gemm_bf16_kernel(GemmArgs p) {
         const char* base = (MODE == MODE_SWIGLU_UP && nf >= NF / 2) ? Wb1 : Wb0;
         rb[slot][s][nf] = *reinterpret_cast<const bf16x8*>(base + (boff[nf] + ko + s * 64));
       }
+  };
+  // Mark a weight slot as consumed on every path (the MFMAs that read it sit behind the
+  // row-count guards), so its registers can be reloaded without a memory wait.
+  auto consume_b = [&](int slot) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int nf = 0; nf < NF; ++nf) asm volatile("" ::"v"(rb[slot][s][nf]));
   };
   auto read_a = [&](int slot, int s, int mf) {
     const int r = mf * 16 + (lane & 15);
@@ -271,36 +285,64 @@ __global__ __launch_bounds__(NW * 64, 1) void ffn_gemm_bf16_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < NF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Multiply one stage.  Activation fragments are read from LDS in groups of GS so one
+  // LDS latency covers GS*NF MFMAs; groups past the tile's last real row are skipped.
+  // Tiles of up to 128 rows also read the next group before the current group's MFMAs
+  // (the 256-row tile has no registers to spare for that).
+  constexpr int GS = MT < 4 ? MT : 4;
+  constexpr int NG = 2 * (MT / GS);          // groups per stage: 2 k32 steps x MT/GS
+  constexpr bool PREFETCH = MT <= 8;
   auto compute = [&](int aslot, int bslot) {
+    bf16x8 a[PREFETCH ? 2 : 1][GS];
+    if (PREFETCH) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+      for (int j = 0; j < GS; ++j) a[0][j] = read_a(aslot, 0, j);
+    }
 #pragma unroll
-      for (int mf = 0; mf < MT; ++mf) {
-        if (mf < nmf) {
-          const bf16x8 a = read_a(aslot, s, mf);
+    for (int q = 0; q < NG; ++q) {
+      const int s = q / (MT / GS), g = q % (MT / GS);
+      const int cur = PREFETCH ? (q & 1) : 0;
+      if (PREFETCH && q + 1 < NG) {
+        const int s1 = (q + 1) / (MT / GS), g1 = (q + 1) % (MT / GS);
+        if (g1 * GS < nmf) {
+#pragma unroll
+          for (int j = 0; j < GS; ++j) a[(q + 1) & 1][j] = read_a(aslot, s1, g1 * GS + j);
+        }
+      }
+      if (g * GS < nmf) {
+        if (!PREFETCH) {
+#pragma unroll
+          for (int j = 0; j < GS; ++j) a[0][j] = read_a(aslot, s, g * GS + j);
+        }
+#pragma unroll
+        for (int j = 0; j < GS; ++j)
 #pragma unroll
           for (int nf = 0; nf < NF; ++nf)
-            acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, rb[bslot][s][nf], acc[mf][nf], 0, 0, 0);
-        }
+            acc[g * GS + j][nf] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[cur][j], rb[bslot][s][nf], acc[g * GS + j][nf], 0, 0, 0);
       }
     }
   };
 
+  // Pipeline.  In the phase of stage st: load activations and weights of stage st+2
+  // (activations first), multiply stage st, store the activations of stage st+1 into LDS,
+  // barrier.  The memory counter is in issue order, so the wait before that store only
+  // covers loads issued up to the previous phase: the weights of stages st+1 and st+2 stay
+  // in flight across it.  Weights use 3 register slots (stage mod 3), activations 2
+  // register slots (stage mod 2) and 3 LDS slots (stage mod 3).  The pipeline starts at
+  // stage -2 so every load is issued inside the loop and the loop-carried memory waits
+  // are exact; base = -2 = 4 (mod 6) keeps every slot index a compile-time constant.
   if (nst > 0) {
-    load_a(0);
-    load_b(0, 0);
-    load_b(1, 1);
-    store_a(0);
-    __syncthreads();
-    for (int base = 0; base < nst; base += RING) {
+    for (int base = -2; base < nst; base += 6) {
 #pragma unroll
-      for (int ph = 0; ph < RING; ++ph) {
+      for (int ph = 0; ph < 6; ++ph) {
         const int st = base + ph;
         if (st >= nst) break;
-        load_a(st + 1);
-        load_b(st + 2, (ph + 2) % RING);
-        compute(ph, ph);
-        store_a((ph + 1) % RING);
+        load_a(st + 2, ph % 2);
+        load_b(st + 2, ph % 3);
+        if (st >= 0) compute((ph + 1) % 3, (ph + 1) % 3);
+        consume_b((ph + 1) % 3);
+        if (st + 1 >= 0) store_a((ph + 1) % 2, (ph + 2) % 3);
         __syncthreads();
       }
     }
