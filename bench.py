@@ -37,9 +37,47 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, help="workload number 1-5 (default 2: prefill, E=64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-experts", type=int, default=8,
+    ap.add_argument("--cpu-experts", type=int, default=1024,
                     help="experts whose rows the CPU oracle computes for its timed sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (3 times): the reference "
+                         "kernel whose FETCH_SIZE / WRITE_SIZE counters calibrate the HBM byte counts")
     return ap.parse_args()
+
+
+FFN_SOURCE = os.path.join(ROOT, "sparse_mixture_experts_27_amd", "csrc", "moe_ffn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_up_prefill_e64_traffic.json")
+
+
+def source_digest(path: str) -> str:
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(cfg_name: str):
+    """HBM bytes per launch of the gate/up GEMM from the committed counter summary, or None
+    when there is none for this workload or the GEMM source changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") != cfg_name or t.get("ffn_source_sha256_16") != source_digest(FFN_SOURCE):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(mib: int):
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read_per_launch": n * 4, "bytes_written_per_launch": n * 4,
+                      "launches": 3}), flush=True)
 
 
 def layer_counts(cfg, L):
@@ -81,9 +119,11 @@ def roofline(bytes_, flops, seconds, dtype):
 
 
 def cpu_baseline(cfg, inp, L, n_exp):
-    """The oracle, as it stands, on a bounded sample: routing and dispatch of all T tokens,
-    then the FFN of every row routed to the first n_exp touched experts and their
-    weighted contribution.  Tokens-equivalent = rows / k."""
+    """The oracle, as it stands, timed on the host cores: routing and dispatch of all T
+    tokens, then, for the first n_exp touched experts (all of them by default), the FFN
+    of every row routed there and its weighted contribution to the output.  Expert
+    weights are converted to float64 outside the timed region.  Tokens-equivalent =
+    rows computed / k."""
     from oracle import moe_oracle as O
     from sparse_mixture_experts_27_amd import synth
     try:
@@ -99,10 +139,11 @@ def cpu_baseline(cfg, inp, L, n_exp):
     idx = O.select_topk(z, cfg.k)
     w = O.topk_weights(z, idx)
     dp = O.dispatch(idx, cfg.E, cfg.capacity)
-    t_route = time.perf_counter() - t0
+    out = np.zeros((cfg.T, cfg.d))
+    t_oracle = time.perf_counter() - t0
     kept = np.diff(dp["offsets"])
     experts = [int(e) for e in np.nonzero(kept)[0][:n_exp]]
-    t_ffn, rows = 0.0, 0
+    rows = 0
     for e in experts:
         wts = (synth.to_numpy(inp["w_gate"][e]),
                None if inp["w_up"] is None else synth.to_numpy(inp["w_up"][e]),
@@ -112,24 +153,27 @@ def cpu_baseline(cfg, inp, L, n_exp):
         tok, j = slots // cfg.k, slots % cfg.k
         t1 = time.perf_counter()
         y = O.expert_ffn(x64[tok], cfg.act, *wts)
-        contrib = w[tok, j][:, None] * y          # this expert's share of the combine
-        t_ffn += time.perf_counter() - t1
+        np.add.at(out, tok, w[tok, j][:, None] * y)          # this expert's share of the combine
+        t_oracle += time.perf_counter() - t1
         rows += len(r)
-        del wts, y, contrib
-    total = t_route + t_ffn
+        del wts, y
     tokens_equiv = rows / cfg.k
-    return dict(value=round(tokens_equiv / total, 2), unit="tokens/s", cores=int(threads), kind="oracle",
-                sample=(f"{cfg.name}: routing+dispatch of all {cfg.T} tokens, FFN+combine of the {rows} rows "
-                        f"routed to {len(experts)} experts (= {tokens_equiv:.0f} token-equivalents), "
-                        f"float64 numpy, {total:.1f} s"),
-                seconds=round(total, 2))
+    whole = len(experts) == int((kept > 0).sum())
+    what = "the whole layer" if whole else f"{rows} of {int(kept.sum())} routed rows ({len(experts)} experts)"
+    return dict(value=round(tokens_equiv / t_oracle, 2), unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=(f"{cfg.name}: routing + dispatch of all {cfg.T} tokens and FFN + combine of {what} "
+                        f"(= {tokens_equiv:.0f} token-equivalents), float64 numpy, {t_oracle:.1f} s of oracle time"),
+                seconds=round(t_oracle, 2))
 
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the layer runs on a single MI355X; see DESIGN.md for how it would shard).", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the layer runs on a "
+              "single MI355X (expert-parallel sharding over several GPUs is designed, not built).", file=sys.stderr)
         sys.exit(2)
     import torch
     from sparse_mixture_experts_27_amd import binding as B
@@ -170,7 +214,7 @@ def main():
     alg = algorithmic(cfg, touched, rows)
     up_s = stage_ms["ffn_up"] / 1e3
     roof = roofline(alg["up_bytes"], alg["up_flops"], up_s, cfg.dtype)
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(cfg.name)
     roof["kernel"] = "ffn_gemm_bf16_kernel<SwiGLU up>" if cfg.dtype == "bf16" else "ffn_gemm_f32_kernel<up>"
     layer_roof = roofline(alg["layer_bytes"], alg["layer_flops"], ms_step / 1e3, cfg.dtype)
     down_roof = roofline(alg["down_bytes"], alg["down_flops"], stage_ms["ffn_down"] / 1e3, cfg.dtype)
