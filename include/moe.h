@@ -78,11 +78,16 @@ const char* moe_last_error(void);
  *            equal logits are ordered by ascending expert index
  *   topk_w   [T, k] fp32 out: routing weights (sum to 1 per token)
  *   logits   [T, E] fp32 out: the router logits (fp32 accumulation)
- * Deterministic: identical inputs give identical bits.
+ *   ws       device workspace of moe_route_workspace_bytes(T, d, E, dt) bytes (may be NULL
+ *            when that is 0): with few tokens the contraction over d is split across
+ *            workgroups and the partial logits are added in a fixed order
+ * Deterministic: identical inputs and sizes give identical bits.
  */
+size_t moe_route_workspace_bytes(int64_t T, int64_t d, int32_t E, moe_dtype_t dt);
 moe_status_t moe_route(const void* x, const void* w_r, const float* bias, moe_dtype_t dt,
                        int64_t T, int64_t d, int32_t E, int32_t k,
-                       int32_t* topk_idx, float* topk_w, float* logits, hipStream_t stream);
+                       int32_t* topk_idx, float* topk_w, float* logits, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
 
 /* Workspace bytes moe_dispatch needs for T tokens and E experts (host, pure). */
 size_t moe_dispatch_workspace_bytes(int64_t T, int32_t E);

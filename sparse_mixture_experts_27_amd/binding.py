@@ -13,7 +13,8 @@ from typing import Optional
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+# MOE_LIBRARY may name another build of the same library (e.g. a tuning variant).
+_LIB_PATH = os.environ.get("MOE_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 _lib = None
 
 MOE_F32, MOE_BF16 = 0, 1
@@ -21,7 +22,8 @@ MOE_ACT_GELU, MOE_ACT_SWIGLU = 0, 1
 STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EUNSUPPORTED", 3: "MOE_EWORKSPACE", 4: "MOE_EHIP"}
 
 # entry points declared in include/moe.h
-EXPORTS = ("moe_status_string", "moe_last_error", "moe_route", "moe_dispatch_workspace_bytes",
+EXPORTS = ("moe_status_string", "moe_last_error", "moe_route_workspace_bytes", "moe_route",
+           "moe_dispatch_workspace_bytes",
            "moe_dispatch", "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine",
            "moe_layer_workspace_bytes", "moe_layer_forward")
 
@@ -67,8 +69,10 @@ def lib():
         L.moe_status_string.argtypes = [C.c_int]
         L.moe_last_error.restype = C.c_char_p
         L.moe_last_error.argtypes = []
+        L.moe_route_workspace_bytes.restype = sz
+        L.moe_route_workspace_bytes.argtypes = [i64, i64, i32, C.c_int]
         L.moe_route.restype = C.c_int
-        L.moe_route.argtypes = [vp, vp, vp, C.c_int, i64, i64, i32, i32, vp, vp, vp, vp]
+        L.moe_route.argtypes = [vp, vp, vp, C.c_int, i64, i64, i32, i32, vp, vp, vp, vp, sz, vp]
         L.moe_dispatch_workspace_bytes.restype = sz
         L.moe_dispatch_workspace_bytes.argtypes = [i64, i32]
         L.moe_dispatch.restype = C.c_int
@@ -137,8 +141,9 @@ def route(x, w_r, k, bias=None):
     idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
     w = torch.empty((T, k), dtype=torch.float32, device=x.device)
     logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    ws = _ws(lib().moe_route_workspace_bytes(T, d, E, _dt(x)), x.device)
     _check(lib().moe_route(_ptr(x), _ptr(w_r), _ptr(bias), _dt(x), T, d, E, k,
-                           _ptr(idx), _ptr(w), _ptr(logits), _stream(x.device)))
+                           _ptr(idx), _ptr(w), _ptr(logits), _ptr(ws), ws.numel(), _stream(x.device)))
     return idx, w, logits
 
 

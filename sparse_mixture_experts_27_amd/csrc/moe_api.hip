@@ -101,12 +101,20 @@ const char* moe_status_string(moe_status_t s) {
 
 const char* moe_last_error(void) { return g_last_error; }
 
+size_t moe_route_workspace_bytes(int64_t T, int64_t d, int32_t E, moe_dtype_t dt) {
+  if (T < 0 || d < 1 || E < 1 || !valid_dt(dt)) return 0;
+  return route_ws_bytes(T, d, E, dt);
+}
+
 moe_status_t moe_route(const void* x, const void* w_r, const float* bias, moe_dtype_t dt, int64_t T, int64_t d,
-                       int32_t E, int32_t k, int32_t* topk_idx, float* topk_w, float* logits,
-                       hipStream_t stream) {
+                       int32_t E, int32_t k, int32_t* topk_idx, float* topk_w, float* logits, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
   g_last_error[0] = 0;
   if (moe_status_t st = check_route_args(x, w_r, dt, T, d, E, k, topk_idx, topk_w, logits)) return st;
-  return launch_route(x, w_r, bias, dt, T, d, E, k, topk_idx, topk_w, logits, stream);
+  const size_t need = route_ws_bytes(T, d, E, dt);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(MOE_EWORKSPACE, "route needs %zu workspace bytes, got %zu", need, ws_bytes);
+  return launch_route(x, w_r, bias, dt, T, d, E, k, topk_idx, topk_w, logits, ws, stream);
 }
 
 size_t moe_dispatch_workspace_bytes(int64_t T, int32_t E) {
@@ -166,7 +174,7 @@ moe_status_t moe_combine(const float* y, int64_t y_rows, const int32_t* inv, con
 
 static size_t layer_layout(const moe_layer_args_t* a, bool carve, WsCarver& c, int32_t** idx, float** w,
                            float** logits, int32_t** counts, int32_t** offsets, int32_t** perm, int32_t** inv,
-                           int32_t** ndrop, void** dws, float** Y, void** fws, FfnPlan* plan) {
+                           int32_t** ndrop, void** rws, void** dws, float** Y, void** fws, FfnPlan* plan) {
   const int64_t T = a->T;
   const bool shared = a->s_gate != nullptr;
   const int64_t max_rows = T * a->k + (shared ? T : 0);
@@ -179,6 +187,7 @@ static size_t layer_layout(const moe_layer_args_t* a, bool carve, WsCarver& c, i
   int32_t* pm = c.take<int32_t>(static_cast<size_t>(T) * a->k);
   int32_t* iv = c.take<int32_t>(static_cast<size_t>(T) * a->k);
   int32_t* nd = c.take<int32_t>(1);
+  void* rw = c.take<char>(route_ws_bytes(T, a->d, a->E, a->dt));
   void* dw = c.take<char>(dispatch_ws_bytes(T, a->E));
   float* yy = c.take<float>(static_cast<size_t>(plan->splits) * max_rows * a->d);
   void* fw = c.take<char>(plan->ws_bytes);
@@ -191,6 +200,7 @@ static size_t layer_layout(const moe_layer_args_t* a, bool carve, WsCarver& c, i
     *perm = a->perm ? a->perm : pm;
     *inv = a->inv ? a->inv : iv;
     *ndrop = a->n_dropped ? a->n_dropped : nd;
+    *rws = rw;
     *dws = dw;
     *Y = yy;
     *fws = fw;
@@ -203,9 +213,9 @@ size_t moe_layer_workspace_bytes(const moe_layer_args_t* a) {
   WsCarver c(nullptr);
   int32_t *i, *cn, *of, *pm, *iv, *nd;
   float *w, *lg, *Y;
-  void *dws, *fws;
+  void *rws, *dws, *fws;
   FfnPlan plan;
-  return layer_layout(a, false, c, &i, &w, &lg, &cn, &of, &pm, &iv, &nd, &dws, &Y, &fws, &plan);
+  return layer_layout(a, false, c, &i, &w, &lg, &cn, &of, &pm, &iv, &nd, &rws, &dws, &Y, &fws, &plan);
 }
 
 moe_status_t moe_layer_forward(const moe_layer_args_t* a, hipStream_t stream) {
@@ -234,9 +244,9 @@ moe_status_t moe_layer_forward(const moe_layer_args_t* a, hipStream_t stream) {
   WsCarver c(a->ws);
   int32_t *idx, *counts, *offsets, *perm, *inv, *ndrop;
   float *w, *logits, *Y;
-  void *dws, *fws;
+  void *rws, *dws, *fws;
   FfnPlan plan;
-  layer_layout(a, true, c, &idx, &w, &logits, &counts, &offsets, &perm, &inv, &ndrop, &dws, &Y, &fws, &plan);
+  layer_layout(a, true, c, &idx, &w, &logits, &counts, &offsets, &perm, &inv, &ndrop, &rws, &dws, &Y, &fws, &plan);
 
   const int64_t T = a->T;
   const bool shared = a->s_gate != nullptr;
@@ -249,7 +259,7 @@ moe_status_t moe_layer_forward(const moe_layer_args_t* a, hipStream_t stream) {
     if (ev) (void)hipEventRecord(static_cast<hipEvent_t>(ev[i]), stream);
   };
   mark(0);
-  if (moe_status_t st = launch_route(a->x, a->w_r, a->bias, a->dt, T, a->d, a->E, a->k, idx, w, logits, stream))
+  if (moe_status_t st = launch_route(a->x, a->w_r, a->bias, a->dt, T, a->d, a->E, a->k, idx, w, logits, rws, stream))
     return st;
   mark(1);
   if (moe_status_t st = launch_dispatch(idx, T, a->E, a->k, capacity, counts, offsets, perm, inv, ndrop, dws, stream))

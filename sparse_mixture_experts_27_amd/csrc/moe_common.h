@@ -7,7 +7,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
-#include "../../include/moe.h"
+#include "moe.h"
 
 namespace moe {
 
@@ -42,9 +42,12 @@ struct WsCarver {
 };
 
 // ---- internal launchers shared between entry points ----------------------------
+// The router splits K over workgroups when there are few token blocks; ws holds the
+// partial logits (route_ws_bytes; 0 when no split is used).
+size_t route_ws_bytes(int64_t T, int64_t d, int E, int dt);
 moe_status_t launch_route(const void* x, const void* w_r, const float* bias, int dt,
                           int64_t T, int64_t d, int E, int k, int32_t* topk_idx,
-                          float* topk_w, float* logits, hipStream_t s);
+                          float* topk_w, float* logits, void* ws, hipStream_t s);
 
 size_t dispatch_ws_bytes(int64_t T, int E);
 moe_status_t launch_dispatch(const int32_t* topk_idx, int64_t T, int E, int k, int64_t capacity,

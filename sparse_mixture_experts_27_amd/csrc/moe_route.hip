@@ -113,14 +113,20 @@ __device__ void finish_tokens(RouteSmem& sm, int64_t tok0, int64_t T, int E, int
   }
 }
 
+// blockIdx.y selects a K range [ky*kchunk, (ky+1)*kchunk).  With one range the kernel
+// finishes the tokens (bias, logits, top-k); with several it writes its partial logits to
+// partial[ky][t][e] and route_finish_kernel adds the ranges in index order.
 __global__ __launch_bounds__(256) void route_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_r, const float* __restrict__ bias,
-    int64_t T, int64_t d, int E, int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    float* __restrict__ logits) {
+    int64_t T, int64_t d, int E, int k, int64_t kchunk, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, float* __restrict__ logits, float* __restrict__ partial) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   RouteSmem sm(smem_raw, E, true);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * RT_TOK;
+  const bool split = gridDim.y > 1;
+  const int64_t kb = static_cast<int64_t>(blockIdx.y) * kchunk;
+  const int64_t ke = kb + kchunk < d ? kb + kchunk : d;
   const int64_t my_tok = tok0 + (lane & 15);
   const bool tok_ok = my_tok < T;
   const uint16_t* xrow = x + (tok_ok ? my_tok : 0) * d;
@@ -131,7 +137,7 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
     f32x4 acc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int64_t k0 = 0; k0 < d; k0 += RT_KC) {
+    for (int64_t k0 = kb; k0 < ke; k0 += RT_KC) {
       __syncthreads();   // previous chunk fully consumed
       // stage W_r[k0 : k0+256, e0 : e0+64] transposed into sm.wt[e][k]
       for (int p = 0; p < RT_KC / 32; ++p) {
@@ -139,14 +145,14 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
         const int ec = (tid & 7) * 8;
         const int64_t kk = k0 + row;
         uint16_t v[8];
-        if (vec_w && kk < d && e0 + ec + 8 <= E) {
+        if (vec_w && kk < ke && e0 + ec + 8 <= E) {
           const u32x4 q = *reinterpret_cast<const u32x4*>(w_r + kk * E + e0 + ec);
 #pragma unroll
           for (int i = 0; i < 4; ++i) { v[2 * i] = q[i] & 0xffff; v[2 * i + 1] = q[i] >> 16; }
         } else {
 #pragma unroll
           for (int i = 0; i < 8; ++i)
-            v[i] = (kk < d && e0 + ec + i < E) ? w_r[kk * E + e0 + ec + i] : 0;
+            v[i] = (kk < ke && e0 + ec + i < E) ? w_r[kk * E + e0 + ec + i] : 0;
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) sm.wt[ec + i][row] = v[i];
@@ -156,14 +162,14 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int kl = wave * 64 + s * 32;
-        const int64_t kb = k0 + kl + 8 * (lane >> 4);
+        const int64_t kx = k0 + kl + 8 * (lane >> 4);
         bf16x8 a;
-        if (tok_ok && vec_x && k0 + kl + 32 <= d) {
-          a = *reinterpret_cast<const bf16x8*>(xrow + kb);
+        if (tok_ok && vec_x && k0 + kl + 32 <= ke) {
+          a = *reinterpret_cast<const bf16x8*>(xrow + kx);
         } else {
           uint16_t v[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) v[i] = (tok_ok && kb + i < d) ? xrow[kb + i] : 0;
+          for (int i = 0; i < 8; ++i) v[i] = (tok_ok && kx + i < ke) ? xrow[kx + i] : 0;
           a = pack_bf16x8(v);
         }
 #pragma unroll
@@ -186,11 +192,40 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
       if (e < E) {
         float z = ((sm.red[0][t][i % RT_EB] + sm.red[1][t][i % RT_EB]) + sm.red[2][t][i % RT_EB]) +
                   sm.red[3][t][i % RT_EB];
-        if (bias) z += bias[e];
-        sm.z[t * E + e] = z;
-        if (tok0 + t < T) logits[(tok0 + t) * E + e] = z;
+        if (split) {
+          if (tok0 + t < T) partial[(static_cast<int64_t>(blockIdx.y) * T + tok0 + t) * E + e] = z;
+        } else {
+          if (bias) z += bias[e];
+          sm.z[t * E + e] = z;
+          if (tok0 + t < T) logits[(tok0 + t) * E + e] = z;
+        }
       }
     }
+  }
+  if (split) return;
+  __syncthreads();
+  finish_tokens(sm, tok0, T, E, k, topk_idx, topk_w);
+}
+
+// Sum the K-range partial logits in range order, add the offsets, finish the tokens.
+__global__ __launch_bounds__(256) void route_finish_kernel(const float* __restrict__ partial, int nsplit,
+                                                           const float* __restrict__ bias, int64_t T, int E,
+                                                           int k, int32_t* __restrict__ topk_idx,
+                                                           float* __restrict__ topk_w, float* __restrict__ logits) {
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  RouteSmem sm(smem_raw, E, false);
+  const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * RT_TOK;
+  for (int i = threadIdx.x; i < RT_TOK * E; i += 256) {
+    const int t = i / E, e = i % E;
+    const int64_t tok = tok0 + t;
+    float z = 0.f;
+    if (tok < T) {
+      z = partial[tok * E + e];
+      for (int s = 1; s < nsplit; ++s) z += partial[(static_cast<int64_t>(s) * T + tok) * E + e];
+      if (bias) z += bias[e];
+      logits[tok * E + e] = z;
+    }
+    sm.z[t * E + e] = z;
   }
   __syncthreads();
   finish_tokens(sm, tok0, T, E, k, topk_idx, topk_w);
@@ -221,23 +256,48 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
 
 }  // namespace
 
+int route_splits(int64_t T, int64_t d, int dt) {
+  if (dt != MOE_BF16) return 1;
+  const int64_t blocks = (T + RT_TOK - 1) / RT_TOK;
+  const int64_t chunks = (d + RT_KC - 1) / RT_KC;
+  int ks = 1;
+  while (blocks * ks < 256 && chunks >= 2 * ks) ks *= 2;
+  return ks;
+}
+
+size_t route_ws_bytes(int64_t T, int64_t d, int E, int dt) {
+  const int ks = route_splits(T, d, dt);
+  return ks > 1 ? static_cast<size_t>(ks) * T * E * sizeof(float) : 0;
+}
+
 moe_status_t launch_route(const void* x, const void* w_r, const float* bias, int dt, int64_t T,
                           int64_t d, int E, int k, int32_t* topk_idx, float* topk_w, float* logits,
-                          hipStream_t s) {
+                          void* ws, hipStream_t s) {
   if (T == 0) return MOE_OK;
   const unsigned grid = static_cast<unsigned>((T + RT_TOK - 1) / RT_TOK);
-  const size_t smem = route_smem_bytes(E, dt == MOE_BF16);
   if (dt == MOE_BF16) {
+    const int ks = route_splits(T, d, dt);
+    const int64_t chunks = (d + RT_KC - 1) / RT_KC;
+    const int64_t kchunk = ((chunks + ks - 1) / ks) * RT_KC;
+    const size_t smem = route_smem_bytes(E, true);
     set_max_dynamic_smem(reinterpret_cast<const void*>(route_bf16_kernel), smem);
-    route_bf16_kernel<<<grid, 256, smem, s>>>(static_cast<const uint16_t*>(x),
-                                              static_cast<const uint16_t*>(w_r), bias, T, d, E, k,
-                                              topk_idx, topk_w, logits);
-  } else {
-    set_max_dynamic_smem(reinterpret_cast<const void*>(route_f32_kernel), smem);
-    route_f32_kernel<<<grid, 256, smem, s>>>(static_cast<const float*>(x),
-                                             static_cast<const float*>(w_r), bias, T, d, E, k,
-                                             topk_idx, topk_w, logits);
+    route_bf16_kernel<<<dim3(grid, ks), 256, smem, s>>>(static_cast<const uint16_t*>(x),
+                                                        static_cast<const uint16_t*>(w_r), bias, T, d, E, k,
+                                                        kchunk, topk_idx, topk_w, logits, static_cast<float*>(ws));
+    if (moe_status_t st = check_launch("route kernel")) return st;
+    if (ks > 1) {
+      const size_t smem2 = route_smem_bytes(E, false);
+      set_max_dynamic_smem(reinterpret_cast<const void*>(route_finish_kernel), smem2);
+      route_finish_kernel<<<grid, 256, smem2, s>>>(static_cast<const float*>(ws), ks, bias, T, E, k, topk_idx,
+                                                   topk_w, logits);
+      return check_launch("route finish kernel");
+    }
+    return MOE_OK;
   }
+  const size_t smem = route_smem_bytes(E, false);
+  set_max_dynamic_smem(reinterpret_cast<const void*>(route_f32_kernel), smem);
+  route_f32_kernel<<<grid, 256, smem, s>>>(static_cast<const float*>(x), static_cast<const float*>(w_r), bias, T,
+                                           d, E, k, topk_idx, topk_w, logits);
   return check_launch("route kernel");
 }
 

@@ -51,7 +51,7 @@ def _route(lib, **kw):
     a = dict(x=16, w_r=16, bias=None, dt=B.MOE_BF16, T=4, d=64, E=8, k=2, idx=16, w=16, logits=16)
     a.update(kw)
     return lib.moe_route(a["x"], a["w_r"], a["bias"], a["dt"], a["T"], a["d"], a["E"], a["k"],
-                         a["idx"], a["w"], a["logits"], None)
+                         a["idx"], a["w"], a["logits"], a.get("ws", 16), a.get("ws_bytes", 1 << 30), None)
 
 
 def test_route_validation(lib):
@@ -68,6 +68,12 @@ def test_route_validation(lib):
     assert _route(lib, x=24) == 1            # misaligned
     assert _route(lib, T=0) == 0             # no-op, nothing launched
     assert lib.moe_last_error() == b""
+    # few tokens split the contraction over workgroups: partial logits need a workspace
+    need = lib.moe_route_workspace_bytes(16, 4096, 64, B.MOE_BF16)
+    assert need == 16 * 16 * 64 * 4
+    assert lib.moe_route_workspace_bytes(4096, 4096, 64, B.MOE_BF16) == 0
+    assert lib.moe_route_workspace_bytes(16, 4096, 64, B.MOE_F32) == 0
+    assert _route(lib, T=16, d=4096, E=64, ws=16, ws_bytes=need - 1) == 3
 
 
 def test_dispatch_validation(lib):
