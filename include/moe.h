@@ -60,6 +60,11 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
 typedef enum { MOE_ACT_GELU = 0, MOE_ACT_SWIGLU = 1 } moe_act_t;
+/* Routing weights of the selected experts:
+ *   MOE_WEIGHTS_RENORMALIZED  w_j = p_{s_j} / sum_{i<k} p_{s_i}   ([mlqm] §3.3, §4.2)
+ *   MOE_WEIGHTS_SOFTMAX       w_j = p_{s_j}, the softmax probabilities themselves
+ *                             ("MoE混合专家架构原理与工程实践…" §3.2: output = p1 e1 + p2 e2) */
+typedef enum { MOE_WEIGHTS_RENORMALIZED = 0, MOE_WEIGHTS_SOFTMAX = 1 } moe_weights_t;
 
 /* Static description of a status code (host). */
 const char* moe_status_string(moe_status_t s);
@@ -76,7 +81,8 @@ const char* moe_last_error(void);
  *   bias     [E] fp32 or NULL (no offsets)
  *   topk_idx [T, k] int32 out: expert of slot j, slots ordered by descending logit;
  *            equal logits are ordered by ascending expert index
- *   topk_w   [T, k] fp32 out: routing weights (sum to 1 per token)
+ *   weights  moe_weights_t: how the selected probabilities become routing weights
+ *   topk_w   [T, k] fp32 out: routing weights (sum to 1 per token when renormalised)
  *   logits   [T, E] fp32 out: the router logits (fp32 accumulation)
  *   ws       device workspace of moe_route_workspace_bytes(T, d, E, dt) bytes (may be NULL
  *            when that is 0): with few tokens the contraction over d is split across
@@ -85,7 +91,7 @@ const char* moe_last_error(void);
  */
 size_t moe_route_workspace_bytes(int64_t T, int64_t d, int32_t E, moe_dtype_t dt);
 moe_status_t moe_route(const void* x, const void* w_r, const float* bias, moe_dtype_t dt,
-                       int64_t T, int64_t d, int32_t E, int32_t k,
+                       int64_t T, int64_t d, int32_t E, int32_t k, moe_weights_t weights,
                        int32_t* topk_idx, float* topk_w, float* logits, void* ws, size_t ws_bytes,
                        hipStream_t stream);
 
@@ -153,12 +159,37 @@ moe_status_t moe_combine(const float* y, int64_t y_rows, const int32_t* inv,
                          const float* topk_w, const float* shared, int64_t T, int64_t d,
                          int32_t k, moe_dtype_t out_dt, void* out, hipStream_t stream);
 
+/* Number of floats moe_routing_stats writes for E experts. */
+#define MOE_STATS_FLOATS(E) (5 + (E))
+
+/* Workspace bytes moe_routing_stats needs for T tokens (host, pure). */
+size_t moe_routing_stats_workspace_bytes(int64_t T);
+
+/*
+ * moe_routing_stats - load-balance terms and monitoring metrics of one batch.
+ *   With u_e = counts[e] / T (the fraction of tokens that selected e; sum_e u_e = k):
+ *   stats[0] balance ratio std(u) / (mean(u) + 1e-8), std with Bessel's correction
+ *            ([mlqm] §4.2 code); stats[1] = lambda_balance * stats[0] ([mlqm] §3.1, 0.01)
+ *   stats[2] L_aux = lambda_aux * (std(u) + gamma_aux * max(u))
+ *            ("MoE混合专家架构原理与工程实践…" §3.2: lambda 0.01, gamma 100)
+ *   stats[3] router entropy: mean over tokens of -sum_e p_e ln p_e, p = softmax(logits)
+ *   stats[4] token drop rate n_dropped / (T k)                ("大模型MoE架构揭秘…" §6.1)
+ *   stats[5 + e] utilization ratio counts[e] / (T k)            ("大模型MoE架构揭秘…" §6.1)
+ *   logits [T, E] fp32, counts [E] int32 (demand, as written by moe_dispatch),
+ *   n_dropped [1] int32 or NULL (0), stats [MOE_STATS_FLOATS(E)] fp32 out.
+ *   Reductions run in a fixed order in double precision: bit-reproducible.
+ */
+moe_status_t moe_routing_stats(const float* logits, const int32_t* counts, const int32_t* n_dropped,
+                               int64_t T, int32_t E, int32_t k, float lambda_balance, float lambda_aux,
+                               float gamma_aux, float* stats, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Arguments of the whole layer (host struct; pointers inside are device pointers). */
 typedef struct moe_layer_args {
   int32_t dt;            /* moe_dtype_t: activations and weights */
   int32_t act;           /* moe_act_t */
   int32_t out_dt;        /* moe_dtype_t of `out`: MOE_F32 (0, the fp32 accumulator rounded
                             once) or MOE_BF16 (rounded once to bf16) */
+  int32_t weights;       /* moe_weights_t (0: renormalised) */
   int64_t T, d, F;
   int32_t E, k;
   int64_t capacity;      /* <= 0: unlimited */
@@ -188,6 +219,10 @@ typedef struct moe_layer_args {
      0 start, 1 route, 2 dispatch, 3 FFN schedule, 4 FFN up-projection (gate/up GEMM),
      5 FFN down-projection, 6 combine.  The library only records them. */
   void* const* stage_events;
+  /* Optional routing statistics (moe_routing_stats layout), computed after dispatch:
+     NULL, or MOE_STATS_FLOATS(E) floats, with the three coefficients below. */
+  float* stats;
+  float lambda_balance, lambda_aux, gamma_aux;
 } moe_layer_args_t;
 
 #define MOE_STAGE_EVENTS 7

@@ -86,14 +86,20 @@ def softmax(z: np.ndarray) -> np.ndarray:
     return ez / ez.sum(axis=1, keepdims=True)
 
 
-def topk_weights(z: np.ndarray, idx: np.ndarray) -> np.ndarray:
-    """Routing weights w_j = p_{s_j} / sum_i p_{s_i} over the selected experts s.
+def topk_weights(z: np.ndarray, idx: np.ndarray, mode: str = "renormalized") -> np.ndarray:
+    """Routing weights of the selected experts s, float64 [T, k].
 
-    [mlqm] §3.3: for top-2, w_i = p_i / (p_i + p_j); [mlqm] §4.2 divides the top-k
-    probabilities by their sum.  Returns float64 [T, k].
+    mode "renormalized" (default): w_j = p_{s_j} / sum_i p_{s_i}.  [mlqm] §3.3: for top-2,
+        w_i = p_i / (p_i + p_j); [mlqm] §4.2 divides the top-k probabilities by their sum.
+    mode "softmax": w_j = p_{s_j}, the softmax probabilities themselves.  [cnnet] §3.2:
+        output = p1 x e1 + p2 x e2; [wmrh] §5.1 weights by the top-k probabilities.
     """
     p = softmax(z)
     sel = np.take_along_axis(p, np.asarray(idx, np.int64), axis=1)
+    if mode == "softmax":
+        return sel
+    if mode != "renormalized":
+        raise ValueError(mode)
     return sel / sel.sum(axis=1, keepdims=True)
 
 
@@ -112,14 +118,16 @@ def topk_margin(z: np.ndarray, k: int) -> np.ndarray:
 # ----------------------------------------------------------------------------------
 # Capacity and dispatch
 # ----------------------------------------------------------------------------------
-def capacity_rule(T: int, k: int, E: int, factor: float = 1.0) -> int:
-    """Per-expert capacity C = factor * T * k / E, rounded up.
+def capacity_rule(T: int, k: int, E: int, factor: float = 1.0, min_capacity: int = 0) -> int:
+    """Per-expert capacity C = max(min_capacity, ceil(factor * T * k / E)).
 
     [rkmt] §2.3: with 1024 tokens, K=2 and 16 experts the capacity is (1024x2)/16 = 128.
     The page's example divides exactly; for a non-integral quotient the ceiling is taken
-    so that a perfectly balanced load never drops a token.
+    so that a perfectly balanced load never drops a token.  [cnnet] §4.2 (DeepSpeed-MoE
+    block): capacity_factor 1.2 in training, eval_capacity_factor 2.0 at inference, and
+    min_capacity 4 as a floor for tiny batches.
     """
-    return int(math.ceil(factor * T * k / E))
+    return max(int(min_capacity), int(math.ceil(factor * T * k / E)))
 
 
 def dispatch(idx: np.ndarray, E: int, capacity: int = 0) -> Dict[str, np.ndarray]:
@@ -253,7 +261,7 @@ def routed_output(x_rows: np.ndarray, idx_rows: np.ndarray, w_rows: np.ndarray,
 def moe_layer(x: np.ndarray, w_r: np.ndarray, k: int, act: str,
               w_gate: np.ndarray, w_up: Optional[np.ndarray], w_down: np.ndarray,
               bias: Optional[np.ndarray] = None, capacity: int = 0,
-              shared: Optional[ExpertWeights] = None) -> Dict[str, np.ndarray]:
+              shared: Optional[ExpertWeights] = None, weights: str = "renormalized") -> Dict[str, np.ndarray]:
     """Whole layer: router -> top-k -> weights -> capacity/dispatch -> experts -> combine.
 
     Follows [mlqm] §3.1-§3.3 and §4.2, [rkmt] §2.3 and [200B-5].  Stacked expert weights:
@@ -263,7 +271,7 @@ def moe_layer(x: np.ndarray, w_r: np.ndarray, k: int, act: str,
     E = np.asarray(w_r).shape[1]
     z = router_logits(x, w_r, bias)
     idx = select_topk(z, k)
-    w = topk_weights(z, idx)
+    w = topk_weights(z, idx, weights)
     disp = dispatch(idx, E, capacity)
     keep = disp["inv"] >= 0
     out = routed_output(
@@ -291,3 +299,39 @@ def expert_weight_bytes(E: int, d: int, F: int, act: str, bytes_per_elem: int) -
     """Bytes of E stacked experts: 3 d F weights each for SwiGLU, 2 d F for GeLU."""
     mats = 3 if act == "swiglu" else 2
     return E * mats * d * F * bytes_per_elem
+
+
+# ----------------------------------------------------------------------------------
+# Routing statistics (monitoring and load-balance terms of one forward pass)
+# ----------------------------------------------------------------------------------
+def routing_stats(z: np.ndarray, counts: np.ndarray, n_dropped: int, k: int,
+                  lambda_balance: float = 0.01, lambda_aux: float = 0.01, gamma_aux: float = 100.0
+                  ) -> Dict[str, np.ndarray]:
+    """Load-balance and monitoring statistics of one batch.
+
+    u_e = counts_e / T, the fraction of tokens that selected expert e ([mlqm] §4.2: the
+    mean over tokens of the summed one-hot selection mask; sum_e u_e = k).
+      balance_ratio = std(u) / (mean(u) + 1e-8), std with Bessel's correction ([mlqm]
+                      §4.2 code); L_balance = lambda_balance * balance_ratio ([mlqm] §3.1,
+                      lambda = 0.01)
+      l_aux         = lambda_aux * (std(u) + gamma_aux * max(u)) ([cnnet] §3.2, lambda = 0.01,
+                      gamma = 100)
+      utilization   = counts_e / (T k), each expert's share of all selections ([rkmt] §6.1;
+                      16 balanced experts take 6.25% each, [rkmt] §2.3)
+      drop_rate     = dropped slots / (T k) ([rkmt] §6.1 token_drop_rate)
+      entropy       = mean over tokens of -sum_e p_e ln p_e, p = softmax(z) ([rkmt] §6.1
+                      router_entropy; natural logarithm)
+    """
+    z64 = np.asarray(z, F64)
+    T, E = z64.shape
+    counts = np.asarray(counts, F64)
+    u = counts / T
+    std = float(np.std(u, ddof=1)) if E > 1 else 0.0
+    ratio = std / (float(np.mean(u)) + 1e-8)
+    p = softmax(z64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        plogp = np.where(p > 0, p * np.log(p), 0.0)
+    entropy = float(np.mean(-plogp.sum(axis=1)))
+    return dict(balance_ratio=ratio, l_balance=lambda_balance * ratio,
+                l_aux=lambda_aux * (std + gamma_aux * float(np.max(u))),
+                utilization=counts / (T * k), drop_rate=n_dropped / (T * k), entropy=entropy)

@@ -19,12 +19,14 @@ _lib = None
 
 MOE_F32, MOE_BF16 = 0, 1
 MOE_ACT_GELU, MOE_ACT_SWIGLU = 0, 1
+WEIGHT_MODES = {"renormalized": 0, "softmax": 1}
 STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EUNSUPPORTED", 3: "MOE_EWORKSPACE", 4: "MOE_EHIP"}
 
 # entry points declared in include/moe.h
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_route_workspace_bytes", "moe_route",
            "moe_dispatch_workspace_bytes",
            "moe_dispatch", "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine",
+           "moe_routing_stats_workspace_bytes", "moe_routing_stats",
            "moe_layer_workspace_bytes", "moe_layer_forward")
 
 
@@ -35,7 +37,7 @@ class MoEError(RuntimeError):
 
 
 class LayerArgs(C.Structure):
-    _fields_ = [("dt", C.c_int32), ("act", C.c_int32), ("out_dt", C.c_int32),
+    _fields_ = [("dt", C.c_int32), ("act", C.c_int32), ("out_dt", C.c_int32), ("weights", C.c_int32),
                 ("T", C.c_int64), ("d", C.c_int64), ("F", C.c_int64),
                 ("E", C.c_int32), ("k", C.c_int32), ("capacity", C.c_int64),
                 ("x", C.c_void_p), ("w_r", C.c_void_p), ("bias", C.c_void_p),
@@ -46,7 +48,11 @@ class LayerArgs(C.Structure):
                 ("counts", C.c_void_p), ("offsets", C.c_void_p), ("perm", C.c_void_p),
                 ("inv", C.c_void_p), ("n_dropped", C.c_void_p),
                 ("ws", C.c_void_p), ("ws_bytes", C.c_size_t),
-                ("stage_events", C.POINTER(C.c_void_p))]
+                ("stage_events", C.POINTER(C.c_void_p)),
+                ("stats", C.c_void_p), ("lambda_balance", C.c_float), ("lambda_aux", C.c_float),
+                ("gamma_aux", C.c_float)]
+
+STAT_NAMES = ("balance_ratio", "l_balance", "l_aux", "entropy", "drop_rate")
 
 STAGE_EVENTS = 7
 STAGES = ("route", "dispatch", "ffn_schedule", "ffn_up", "ffn_down", "combine")
@@ -72,7 +78,7 @@ def lib():
         L.moe_route_workspace_bytes.restype = sz
         L.moe_route_workspace_bytes.argtypes = [i64, i64, i32, C.c_int]
         L.moe_route.restype = C.c_int
-        L.moe_route.argtypes = [vp, vp, vp, C.c_int, i64, i64, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.moe_route.argtypes = [vp, vp, vp, C.c_int, i64, i64, i32, i32, C.c_int, vp, vp, vp, vp, sz, vp]
         L.moe_dispatch_workspace_bytes.restype = sz
         L.moe_dispatch_workspace_bytes.argtypes = [i64, i32]
         L.moe_dispatch.restype = C.c_int
@@ -84,6 +90,10 @@ def lib():
                                      vp, vp, vp, vp, vp, sz, vp]
         L.moe_combine.restype = C.c_int
         L.moe_combine.argtypes = [vp, i64, vp, vp, vp, i64, i64, i32, C.c_int, vp, vp]
+        L.moe_routing_stats_workspace_bytes.restype = sz
+        L.moe_routing_stats_workspace_bytes.argtypes = [i64]
+        L.moe_routing_stats.restype = C.c_int
+        L.moe_routing_stats.argtypes = [vp, vp, vp, i64, i32, i32, C.c_float, C.c_float, C.c_float, vp, vp, sz, vp]
         L.moe_layer_workspace_bytes.restype = sz
         L.moe_layer_workspace_bytes.argtypes = [C.POINTER(LayerArgs)]
         L.moe_layer_forward.restype = C.c_int
@@ -131,7 +141,7 @@ def _ws(nbytes: int, device) -> torch.Tensor:
 
 
 # ------------------------------------------------------------------------------------
-def route(x, w_r, k, bias=None):
+def route(x, w_r, k, bias=None, weights="renormalized"):
     """-> (topk_idx int32 [T,k], topk_w f32 [T,k], logits f32 [T,E])."""
     T, d = x.shape
     E = w_r.shape[1]
@@ -142,7 +152,7 @@ def route(x, w_r, k, bias=None):
     w = torch.empty((T, k), dtype=torch.float32, device=x.device)
     logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
     ws = _ws(lib().moe_route_workspace_bytes(T, d, E, _dt(x)), x.device)
-    _check(lib().moe_route(_ptr(x), _ptr(w_r), _ptr(bias), _dt(x), T, d, E, k,
+    _check(lib().moe_route(_ptr(x), _ptr(w_r), _ptr(bias), _dt(x), T, d, E, k, WEIGHT_MODES[weights],
                            _ptr(idx), _ptr(w), _ptr(logits), _ptr(ws), ws.numel(), _stream(x.device)))
     return idx, w, logits
 
@@ -205,6 +215,20 @@ def combine(y, inv, topk_w, out_dtype, shared=None):
     return out
 
 
+def routing_stats(logits, counts, n_dropped, k, lambda_balance=0.01, lambda_aux=0.01, gamma_aux=100.0):
+    """-> f32 [5 + E]: balance ratio, L_balance, L_aux, entropy, drop rate, utilization[E]."""
+    T, E = logits.shape
+    dev = logits.device
+    _req(logits, "logits", torch.float32, dev)
+    _req(counts, "counts", torch.int32, dev)
+    _req(n_dropped, "n_dropped", torch.int32, dev)
+    stats = torch.empty(5 + E, dtype=torch.float32, device=dev)
+    ws = _ws(lib().moe_routing_stats_workspace_bytes(T), dev)
+    _check(lib().moe_routing_stats(_ptr(logits), _ptr(counts), _ptr(n_dropped), T, E, k, lambda_balance,
+                                   lambda_aux, gamma_aux, _ptr(stats), _ptr(ws), ws.numel(), _stream(dev)))
+    return stats
+
+
 class Layer:
     """One MoE layer with its weights; forward() runs moe_layer_forward.
 
@@ -213,7 +237,8 @@ class Layer:
     """
 
     def __init__(self, w_r, w_gate, w_up, w_down, k, act="swiglu", bias=None, capacity=0,
-                 s_gate=None, s_up=None, s_down=None, out_dtype=torch.float32):
+                 s_gate=None, s_up=None, s_down=None, out_dtype=torch.float32, stats=False,
+                 lambda_balance=0.01, lambda_aux=0.01, gamma_aux=100.0, weights="renormalized"):
         self.w_r, self.bias = w_r, bias
         self.w_gate, self.w_up, self.w_down = w_gate, w_up, w_down
         self.s_gate, self.s_up, self.s_down = s_gate, s_up, s_down
@@ -221,6 +246,9 @@ class Layer:
         if out_dtype not in (torch.float32, torch.bfloat16):
             raise TypeError("out_dtype must be float32 or bfloat16")
         self.out_dtype = out_dtype
+        self.want_stats = bool(stats)
+        self.weight_mode = WEIGHT_MODES[weights]
+        self.stat_coeffs = (lambda_balance, lambda_aux, gamma_aux)
         self.act = MOE_ACT_SWIGLU if act == "swiglu" else MOE_ACT_GELU
         self.E = w_r.shape[1]
         self.F, self.d = w_gate.shape[1], w_gate.shape[2]
@@ -236,10 +264,14 @@ class Layer:
         a = LayerArgs()
         a.dt, a.act = _dt(x), self.act
         a.out_dt = MOE_BF16 if self.out_dtype == torch.bfloat16 else MOE_F32
+        a.weights = self.weight_mode
         a.T, a.d, a.F, a.E, a.k, a.capacity = T, self.d, self.F, self.E, self.k, self.capacity
         a.x, a.w_r, a.bias = _ptr(x), _ptr(self.w_r), _ptr(self.bias)
         a.w_gate, a.w_up, a.w_down = _ptr(self.w_gate), _ptr(self.w_up), _ptr(self.w_down)
         a.s_gate, a.s_up, a.s_down = _ptr(self.s_gate), _ptr(self.s_up), _ptr(self.s_down)
+        if self.want_stats:
+            a.stats = _ptr(self.stats)
+            a.lambda_balance, a.lambda_aux, a.gamma_aux = self.stat_coeffs
         return a
 
     def _buffers(self, x):
@@ -255,6 +287,8 @@ class Layer:
         self.perm = torch.empty(T * k, dtype=torch.int32, device=dev)
         self.inv = torch.empty((T, k), dtype=torch.int32, device=dev)
         self.n_dropped = torch.empty(1, dtype=torch.int32, device=dev)
+        if self.want_stats:
+            self.stats = torch.empty(5 + self.E, dtype=torch.float32, device=dev)
         self.ws = _ws(lib().moe_layer_workspace_bytes(C.byref(self._args(x))), dev)
         self._T, self._dev, self._dtype = T, dev, x.dtype
 

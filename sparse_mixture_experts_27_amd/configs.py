@@ -24,6 +24,7 @@ class MoEConfig:
     shared: bool = False    # one always-on shared expert
     capacity: int = 0       # per-expert capacity, 0 = unlimited
     bias_var: float = 0.0   # variance of the per-expert router offsets, 0 = no offsets
+    weights: str = "renormalized"   # "renormalized" | "softmax": routing-weight formulation
 
     def scaled(self, **kw) -> "MoEConfig":
         return replace(self, **kw)
@@ -32,7 +33,8 @@ class MoEConfig:
     def label(self) -> str:
         return (f"{self.name}(T={self.T},d={self.d},E={self.E}{'+1' if self.shared else ''},"
                 f"k={self.k},F={self.F},{self.act},{self.dtype}"
-                f"{',C=%d' % self.capacity if self.capacity else ''})")
+                f"{',C=%d' % self.capacity if self.capacity else ''}"
+                f"{',w=' + self.weights if self.weights != 'renormalized' else ''})")
 
 
 CONFIGS = {

@@ -107,14 +107,16 @@ size_t moe_route_workspace_bytes(int64_t T, int64_t d, int32_t E, moe_dtype_t dt
 }
 
 moe_status_t moe_route(const void* x, const void* w_r, const float* bias, moe_dtype_t dt, int64_t T, int64_t d,
-                       int32_t E, int32_t k, int32_t* topk_idx, float* topk_w, float* logits, void* ws,
-                       size_t ws_bytes, hipStream_t stream) {
+                       int32_t E, int32_t k, moe_weights_t weights, int32_t* topk_idx, float* topk_w, float* logits,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
   g_last_error[0] = 0;
   if (moe_status_t st = check_route_args(x, w_r, dt, T, d, E, k, topk_idx, topk_w, logits)) return st;
+  if (weights != MOE_WEIGHTS_RENORMALIZED && weights != MOE_WEIGHTS_SOFTMAX)
+    return fail(MOE_EINVAL, "weights mode %d invalid", weights);
   const size_t need = route_ws_bytes(T, d, E, dt);
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(MOE_EWORKSPACE, "route needs %zu workspace bytes, got %zu", need, ws_bytes);
-  return launch_route(x, w_r, bias, dt, T, d, E, k, topk_idx, topk_w, logits, ws, stream);
+  return launch_route(x, w_r, bias, dt, T, d, E, k, weights, topk_idx, topk_w, logits, ws, stream);
 }
 
 size_t moe_dispatch_workspace_bytes(int64_t T, int32_t E) {
@@ -172,9 +174,23 @@ moe_status_t moe_combine(const float* y, int64_t y_rows, const int32_t* inv, con
   return launch_combine(y, y_rows, 1, 0, inv, topk_w, shared, T, d, k, out_dt, out, stream);
 }
 
+size_t moe_routing_stats_workspace_bytes(int64_t T) { return T < 0 ? 0 : stats_ws_bytes(T); }
+
+moe_status_t moe_routing_stats(const float* logits, const int32_t* counts, const int32_t* n_dropped, int64_t T,
+                               int32_t E, int32_t k, float lambda_balance, float lambda_aux, float gamma_aux,
+                               float* stats, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_last_error[0] = 0;
+  if (T < 0 || E < 1 || E > kMaxExperts || k < 1 || k > E) return fail(MOE_EINVAL, "bad sizes (T, E, k)");
+  if (T > 0 && (!logits || !counts || !stats || !ws)) return fail(MOE_EINVAL, "moe_routing_stats: null required pointer");
+  const size_t need = stats_ws_bytes(T);
+  if (ws_bytes < need) return fail(MOE_EWORKSPACE, "routing stats need %zu workspace bytes, got %zu", need, ws_bytes);
+  return launch_stats(logits, counts, n_dropped, T, E, k, lambda_balance, lambda_aux, gamma_aux, stats, ws, stream);
+}
+
 static size_t layer_layout(const moe_layer_args_t* a, bool carve, WsCarver& c, int32_t** idx, float** w,
                            float** logits, int32_t** counts, int32_t** offsets, int32_t** perm, int32_t** inv,
-                           int32_t** ndrop, void** rws, void** dws, float** Y, void** fws, FfnPlan* plan) {
+                           int32_t** ndrop, void** rws, void** sws, void** dws, float** Y, void** fws,
+                           FfnPlan* plan) {
   const int64_t T = a->T;
   const bool shared = a->s_gate != nullptr;
   const int64_t max_rows = T * a->k + (shared ? T : 0);
@@ -188,6 +204,7 @@ static size_t layer_layout(const moe_layer_args_t* a, bool carve, WsCarver& c, i
   int32_t* iv = c.take<int32_t>(static_cast<size_t>(T) * a->k);
   int32_t* nd = c.take<int32_t>(1);
   void* rw = c.take<char>(route_ws_bytes(T, a->d, a->E, a->dt));
+  void* sw = c.take<char>(a->stats ? stats_ws_bytes(T) : 0);
   void* dw = c.take<char>(dispatch_ws_bytes(T, a->E));
   float* yy = c.take<float>(static_cast<size_t>(plan->splits) * max_rows * a->d);
   void* fw = c.take<char>(plan->ws_bytes);
@@ -201,6 +218,7 @@ static size_t layer_layout(const moe_layer_args_t* a, bool carve, WsCarver& c, i
     *inv = a->inv ? a->inv : iv;
     *ndrop = a->n_dropped ? a->n_dropped : nd;
     *rws = rw;
+    *sws = sw;
     *dws = dw;
     *Y = yy;
     *fws = fw;
@@ -213,9 +231,9 @@ size_t moe_layer_workspace_bytes(const moe_layer_args_t* a) {
   WsCarver c(nullptr);
   int32_t *i, *cn, *of, *pm, *iv, *nd;
   float *w, *lg, *Y;
-  void *rws, *dws, *fws;
+  void *rws, *sws, *dws, *fws;
   FfnPlan plan;
-  return layer_layout(a, false, c, &i, &w, &lg, &cn, &of, &pm, &iv, &nd, &rws, &dws, &Y, &fws, &plan);
+  return layer_layout(a, false, c, &i, &w, &lg, &cn, &of, &pm, &iv, &nd, &rws, &sws, &dws, &Y, &fws, &plan);
 }
 
 moe_status_t moe_layer_forward(const moe_layer_args_t* a, hipStream_t stream) {
@@ -224,6 +242,8 @@ moe_status_t moe_layer_forward(const moe_layer_args_t* a, hipStream_t stream) {
   if (moe_status_t st = check_route_args(a->x, a->w_r, a->dt, a->T, a->d, a->E, a->k, a->x, a->x, a->x)) return st;
   if (!valid_act(a->act)) return fail(MOE_EINVAL, "activation %d invalid", a->act);
   if (!valid_dt(a->out_dt)) return fail(MOE_EINVAL, "out dtype %d invalid", a->out_dt);
+  if (a->weights != MOE_WEIGHTS_RENORMALIZED && a->weights != MOE_WEIGHTS_SOFTMAX)
+    return fail(MOE_EINVAL, "weights mode %d invalid", a->weights);
   if (a->F < 1) return fail(MOE_EINVAL, "F must be >= 1");
   if (a->dt == MOE_BF16 && (a->d % 64 != 0 || a->F % 64 != 0))
     return fail(MOE_EUNSUPPORTED, "bf16 layer needs d and F multiples of 64");
@@ -244,9 +264,10 @@ moe_status_t moe_layer_forward(const moe_layer_args_t* a, hipStream_t stream) {
   WsCarver c(a->ws);
   int32_t *idx, *counts, *offsets, *perm, *inv, *ndrop;
   float *w, *logits, *Y;
-  void *rws, *dws, *fws;
+  void *rws, *sws, *dws, *fws;
   FfnPlan plan;
-  layer_layout(a, true, c, &idx, &w, &logits, &counts, &offsets, &perm, &inv, &ndrop, &rws, &dws, &Y, &fws, &plan);
+  layer_layout(a, true, c, &idx, &w, &logits, &counts, &offsets, &perm, &inv, &ndrop, &rws, &sws, &dws, &Y, &fws,
+               &plan);
 
   const int64_t T = a->T;
   const bool shared = a->s_gate != nullptr;
@@ -259,11 +280,17 @@ moe_status_t moe_layer_forward(const moe_layer_args_t* a, hipStream_t stream) {
     if (ev) (void)hipEventRecord(static_cast<hipEvent_t>(ev[i]), stream);
   };
   mark(0);
-  if (moe_status_t st = launch_route(a->x, a->w_r, a->bias, a->dt, T, a->d, a->E, a->k, idx, w, logits, rws, stream))
+  if (moe_status_t st = launch_route(a->x, a->w_r, a->bias, a->dt, T, a->d, a->E, a->k, a->weights, idx, w, logits,
+                                     rws, stream))
     return st;
   mark(1);
   if (moe_status_t st = launch_dispatch(idx, T, a->E, a->k, capacity, counts, offsets, perm, inv, ndrop, dws, stream))
     return st;
+  if (a->stats) {
+    if (moe_status_t st = launch_stats(logits, counts, ndrop, T, a->E, a->k, a->lambda_balance, a->lambda_aux,
+                                       a->gamma_aux, a->stats, sws, stream))
+      return st;
+  }
   mark(2);
   FfnProblem p{};
   p.x = a->x; p.perm = perm; p.k = a->k; p.offsets = offsets; p.G = a->E; p.max_rows = max_rows;

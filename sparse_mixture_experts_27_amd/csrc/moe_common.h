@@ -46,7 +46,7 @@ struct WsCarver {
 // partial logits (route_ws_bytes; 0 when no split is used).
 size_t route_ws_bytes(int64_t T, int64_t d, int E, int dt);
 moe_status_t launch_route(const void* x, const void* w_r, const float* bias, int dt,
-                          int64_t T, int64_t d, int E, int k, int32_t* topk_idx,
+                          int64_t T, int64_t d, int E, int k, int mode, int32_t* topk_idx,
                           float* topk_w, float* logits, void* ws, hipStream_t s);
 
 size_t dispatch_ws_bytes(int64_t T, int E);
@@ -87,6 +87,11 @@ FfnPlan ffn_plan(int64_t max_rows, int G, bool has_shared, int64_t d, int64_t F,
 // ev (nullable): events recorded after the schedule, up-projection and down-projection.
 moe_status_t launch_ffn(const FfnProblem& p, const FfnPlan& plan, float* y, bool reduce_splits,
                         void* ws, hipStream_t s, void* const* ev = nullptr);
+
+size_t stats_ws_bytes(int64_t T);
+moe_status_t launch_stats(const float* logits, const int32_t* counts, const int32_t* n_dropped, int64_t T, int E,
+                          int k, float lambda_balance, float lambda_aux, float gamma_aux, float* stats, void* ws,
+                          hipStream_t s);
 
 moe_status_t launch_combine(const float* y, int64_t y_rows, int nsplit, int64_t split_stride,
                             const int32_t* inv, const float* topk_w, const float* shared,

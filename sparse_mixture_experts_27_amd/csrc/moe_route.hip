@@ -63,7 +63,7 @@ __device__ __forceinline__ float key_to_float(uint32_t o) {
 
 // Top-k of one token's logits zrow[0..E) by one wave; writes idx/w rows.  zs is this
 // wave's LDS row for the selected logits.
-__device__ void topk_one_token(const float* zrow, float* zs, int E, int k, int32_t* idx_out,
+__device__ void topk_one_token(const float* zrow, float* zs, int E, int k, int mode, int32_t* idx_out,
                                float* w_out) {
   const int lane = threadIdx.x & 63;
   const int per_lane = (E + 63) / 64;      // <= 16
@@ -93,10 +93,16 @@ __device__ void topk_one_token(const float* zrow, float* zs, int E, int k, int32
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  // w_j = exp(z_j - z_0) / sum_i exp(z_i - z_0); fixed butterfly order
+  // renormalised: w_j = exp(z_j - z_0) / sum_{i<k} exp(z_i - z_0)
+  // softmax mode:  w_j = exp(z_j - z_0) / sum_{all e} exp(z_e - z_0)   (z_0 is the max)
+  // fixed butterfly order in both
   const float z0 = zs[0];
   float part = 0.f;
-  for (int j = lane; j < k; j += 64) part += expf(zs[j] - z0);
+  if (mode == MOE_WEIGHTS_SOFTMAX) {
+    for (int e = lane; e < E; e += 64) part += expf(zrow[e] - z0);
+  } else {
+    for (int j = lane; j < k; j += 64) part += expf(zs[j] - z0);
+  }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
   const float inv = 1.0f / part;
@@ -104,12 +110,12 @@ __device__ void topk_one_token(const float* zrow, float* zs, int E, int k, int32
   __builtin_amdgcn_wave_barrier();
 }
 
-__device__ void finish_tokens(RouteSmem& sm, int64_t tok0, int64_t T, int E, int k,
+__device__ void finish_tokens(RouteSmem& sm, int64_t tok0, int64_t T, int E, int k, int mode,
                               int32_t* topk_idx, float* topk_w) {
   const int wave = threadIdx.x >> 6;
   for (int t = wave; t < RT_TOK; t += 4) {
     const int64_t tok = tok0 + t;
-    if (tok < T) topk_one_token(sm.z + t * E, sm.zs + wave * E, E, k, topk_idx + tok * k, topk_w + tok * k);
+    if (tok < T) topk_one_token(sm.z + t * E, sm.zs + wave * E, E, k, mode, topk_idx + tok * k, topk_w + tok * k);
   }
 }
 
@@ -118,7 +124,7 @@ __device__ void finish_tokens(RouteSmem& sm, int64_t tok0, int64_t T, int E, int
 // partial[ky][t][e] and route_finish_kernel adds the ranges in index order.
 __global__ __launch_bounds__(256) void route_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_r, const float* __restrict__ bias,
-    int64_t T, int64_t d, int E, int k, int64_t kchunk, int32_t* __restrict__ topk_idx,
+    int64_t T, int64_t d, int E, int k, int mode, int64_t kchunk, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, float* __restrict__ logits, float* __restrict__ partial) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   RouteSmem sm(smem_raw, E, true);
@@ -204,13 +210,13 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
   }
   if (split) return;
   __syncthreads();
-  finish_tokens(sm, tok0, T, E, k, topk_idx, topk_w);
+  finish_tokens(sm, tok0, T, E, k, mode, topk_idx, topk_w);
 }
 
 // Sum the K-range partial logits in range order, add the offsets, finish the tokens.
 __global__ __launch_bounds__(256) void route_finish_kernel(const float* __restrict__ partial, int nsplit,
                                                            const float* __restrict__ bias, int64_t T, int E,
-                                                           int k, int32_t* __restrict__ topk_idx,
+                                                           int k, int mode, int32_t* __restrict__ topk_idx,
                                                            float* __restrict__ topk_w, float* __restrict__ logits) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   RouteSmem sm(smem_raw, E, false);
@@ -228,12 +234,12 @@ __global__ __launch_bounds__(256) void route_finish_kernel(const float* __restri
     sm.z[t * E + e] = z;
   }
   __syncthreads();
-  finish_tokens(sm, tok0, T, E, k, topk_idx, topk_w);
+  finish_tokens(sm, tok0, T, E, k, mode, topk_idx, topk_w);
 }
 
 __global__ __launch_bounds__(256) void route_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ w_r, const float* __restrict__ bias,
-    int64_t T, int64_t d, int E, int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    int64_t T, int64_t d, int E, int k, int mode, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     float* __restrict__ logits) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   RouteSmem sm(smem_raw, E, false);
@@ -251,7 +257,7 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
     sm.z[t * E + e] = z;
   }
   __syncthreads();
-  finish_tokens(sm, tok0, T, E, k, topk_idx, topk_w);
+  finish_tokens(sm, tok0, T, E, k, mode, topk_idx, topk_w);
 }
 
 }  // namespace
@@ -271,7 +277,7 @@ size_t route_ws_bytes(int64_t T, int64_t d, int E, int dt) {
 }
 
 moe_status_t launch_route(const void* x, const void* w_r, const float* bias, int dt, int64_t T,
-                          int64_t d, int E, int k, int32_t* topk_idx, float* topk_w, float* logits,
+                          int64_t d, int E, int k, int mode, int32_t* topk_idx, float* topk_w, float* logits,
                           void* ws, hipStream_t s) {
   if (T == 0) return MOE_OK;
   const unsigned grid = static_cast<unsigned>((T + RT_TOK - 1) / RT_TOK);
@@ -283,12 +289,12 @@ moe_status_t launch_route(const void* x, const void* w_r, const float* bias, int
     set_max_dynamic_smem(reinterpret_cast<const void*>(route_bf16_kernel), smem);
     route_bf16_kernel<<<dim3(grid, ks), 256, smem, s>>>(static_cast<const uint16_t*>(x),
                                                         static_cast<const uint16_t*>(w_r), bias, T, d, E, k,
-                                                        kchunk, topk_idx, topk_w, logits, static_cast<float*>(ws));
+                                                        mode, kchunk, topk_idx, topk_w, logits, static_cast<float*>(ws));
     if (moe_status_t st = check_launch("route kernel")) return st;
     if (ks > 1) {
       const size_t smem2 = route_smem_bytes(E, false);
       set_max_dynamic_smem(reinterpret_cast<const void*>(route_finish_kernel), smem2);
-      route_finish_kernel<<<grid, 256, smem2, s>>>(static_cast<const float*>(ws), ks, bias, T, E, k, topk_idx,
+      route_finish_kernel<<<grid, 256, smem2, s>>>(static_cast<const float*>(ws), ks, bias, T, E, k, mode, topk_idx,
                                                    topk_w, logits);
       return check_launch("route finish kernel");
     }
@@ -297,7 +303,7 @@ moe_status_t launch_route(const void* x, const void* w_r, const float* bias, int
   const size_t smem = route_smem_bytes(E, false);
   set_max_dynamic_smem(reinterpret_cast<const void*>(route_f32_kernel), smem);
   route_f32_kernel<<<grid, 256, smem, s>>>(static_cast<const float*>(x), static_cast<const float*>(w_r), bias, T,
-                                           d, E, k, topk_idx, topk_w, logits);
+                                           d, E, k, mode, topk_idx, topk_w, logits);
   return check_launch("route kernel");
 }
 

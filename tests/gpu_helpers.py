@@ -40,7 +40,7 @@ def say(msg: str):
 def layer_for(cfg, inp, out_dtype=torch.float32):
     return B.Layer(inp["w_r"], inp["w_gate"], inp["w_up"], inp["w_down"], cfg.k, act=cfg.act,
                    bias=inp["bias"], capacity=cfg.capacity, s_gate=inp["s_gate"], s_up=inp["s_up"],
-                   s_down=inp["s_down"], out_dtype=out_dtype)
+                   s_down=inp["s_down"], out_dtype=out_dtype, weights=cfg.weights)
 
 
 def half_ulp_bf16(v: np.ndarray) -> np.ndarray:
@@ -103,7 +103,7 @@ def check_route(cfg, x64, w_r64, bias64, res, report: dict):
     clear = np.all(-np.diff(zs, axis=1) > MARGIN, axis=1) & ~flip
     assert np.array_equal(res["idx"][clear], idx_o[clear]), "slot order differs on clear tokens"
     # weights keyed by expert
-    w_o = O.topk_weights(z_o, res["idx"])
+    w_o = O.topk_weights(z_o, res["idx"], cfg.weights)
     assert np.abs(res["w"] - w_o)[~flip].max(initial=0.0) <= 1e-5, "routing weights differ"
     report.update(route_flips=int(flip.sum()), min_margin=float(margin.min()),
                   max_logit_rel=float(rel.max()))
@@ -126,7 +126,7 @@ def check_output(cfg, x64, z_o, res, fetch, shared, tokens: Optional[np.ndarray]
     """FFN + combine on the GPU's routing, for `tokens` (None = all)."""
     idx = res["idx"]
     keep = res["inv"] >= 0
-    w_o = O.topk_weights(z_o, idx)
+    w_o = O.topk_weights(z_o, idx, cfg.weights)
     sel = np.arange(cfg.T) if tokens is None else np.asarray(tokens)
     ref = O.routed_output(x64[sel], idx[sel], w_o[sel], keep[sel], cfg.act, fetch, shared)
     got = res["out"][sel]

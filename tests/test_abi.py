@@ -50,7 +50,7 @@ def test_status_strings(lib):
 def _route(lib, **kw):
     a = dict(x=16, w_r=16, bias=None, dt=B.MOE_BF16, T=4, d=64, E=8, k=2, idx=16, w=16, logits=16)
     a.update(kw)
-    return lib.moe_route(a["x"], a["w_r"], a["bias"], a["dt"], a["T"], a["d"], a["E"], a["k"],
+    return lib.moe_route(a["x"], a["w_r"], a["bias"], a["dt"], a["T"], a["d"], a["E"], a["k"], a.get("mode", 0),
                          a["idx"], a["w"], a["logits"], a.get("ws", 16), a.get("ws_bytes", 1 << 30), None)
 
 
@@ -66,6 +66,7 @@ def test_route_validation(lib):
     assert _route(lib, x=None) == 1
     assert _route(lib, logits=None) == 1
     assert _route(lib, x=24) == 1            # misaligned
+    assert _route(lib, mode=2) == 1          # unknown weights mode
     assert _route(lib, T=0) == 0             # no-op, nothing launched
     assert lib.moe_last_error() == b""
     # few tokens split the contraction over workgroups: partial logits need a workspace

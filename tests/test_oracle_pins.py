@@ -87,6 +87,19 @@ def _worked_layer(act):
     return O.moe_layer(x, w_r, 2, act, wg, wu, wd), g
 
 
+def _worked_layer_args():
+    """(w_r, k, act, wg, wu, wd) of the SwiGLU worked layer, for variants."""
+    g = _golden("worked_combine.json")
+    targets = np.array([g["expert_outputs"][0], [9.0, 9.0, 9.0], g["expert_outputs"][1], [-9.0, 9.0, -9.0]])
+    w_r = np.zeros((3, 4))
+    w_r[0] = [math.log(3.0), -10.0, 0.0, -10.0]
+    wg = np.zeros((4, 1, 3))
+    wg[:, 0, 0] = 1.0
+    wu = wg.copy()
+    wd = targets[:, :, None] / O.silu(np.array(1.0))
+    return w_r, 2, "swiglu", wg, wu, wd
+
+
 def check_worked_layer():
     for act in ("swiglu", "gelu"):
         res, g = _worked_layer(act)
@@ -105,6 +118,27 @@ def check_printed_gate():
     np.testing.assert_allclose(probs, g["top2_probabilities"], rtol=1e-6)
     w = O.topk_weights(z, idx)[0]
     np.testing.assert_allclose(w, np.array([0.85, 0.08]) / 0.93, rtol=1e-6)
+
+
+def check_softmax_weights():
+    """Un-renormalised weights ([cnnet] §3.2 output = p1 e1 + p2 e2; [wmrh] §5.1): the
+    printed probabilities are the weights; with k = E they equal the renormalised ones."""
+    g = _golden("printed_gate.json")
+    z = np.log(np.array([g["gate_probabilities"]])).astype(np.float32)
+    idx = O.select_topk(z, 2)
+    np.testing.assert_allclose(O.topk_weights(z, idx, "softmax")[0], g["top2_probabilities"], rtol=1e-6)
+    rng = _rng(13)
+    z = rng.standard_normal((20, 5)).astype(np.float32)
+    idx = O.select_topk(z, 5)
+    np.testing.assert_allclose(O.topk_weights(z, idx, "softmax"), O.topk_weights(z, idx), rtol=1e-13)
+    idx = O.select_topk(z, 2)
+    assert np.all(O.topk_weights(z, idx, "softmax").sum(axis=1) < 1.0)
+    res, gold = _worked_layer("swiglu")
+    x = np.array([[1.0, 0.0, 0.0]])
+    r2 = O.moe_layer(x, *_worked_layer_args(), weights="softmax")
+    p = O.softmax(O.router_logits(x, _worked_layer_args()[0]))[0]
+    want = p[0] * np.array(gold["expert_outputs"][0]) + p[2] * np.array(gold["expert_outputs"][1])
+    np.testing.assert_allclose(r2["out"][0], want, rtol=1e-6)
 
 
 def check_ln3_weights():
@@ -183,6 +217,10 @@ def check_capacity_rule():
     assert O.capacity_rule(10, 2, 4) == 5
     assert O.capacity_rule(10, 1, 4) == 3          # ceil(2.5)
     assert O.capacity_rule(1000, 2, 16, 1.25) == 157   # ceil(156.25)
+    # DeepSpeed knobs of [cnnet] §4.2: capacity_factor 1.2, eval 2.0, min_capacity 4
+    assert O.capacity_rule(1024, 2, 16, 1.2, 4) == 154   # ceil(153.6)
+    assert O.capacity_rule(1024, 2, 16, 2.0, 4) == 256
+    assert O.capacity_rule(1, 2, 16, 1.2, 4) == 4        # tiny batch: the floor applies
 
 
 def _keep_bruteforce(idx, capacity):
@@ -315,10 +353,50 @@ def check_ledgers():
     assert O.expert_weight_bytes(4, 64, 128, "gelu", 4) == 4 * 2 * 64 * 128 * 4
 
 
-PINS = [check_worked_combine, check_worked_layer, check_printed_gate, check_ln3_weights,
+# ---------------------------------------------------------------------------------
+# Routing statistics
+# ---------------------------------------------------------------------------------
+def check_routing_stats():
+    """Balance ratio against the page's own formulation in torch (one-hot mask summed
+    over slots, mean over tokens, torch.std); entropy against scipy; closed forms for
+    uniform and collapsed routing."""
+    from scipy.stats import entropy as sp_entropy
+    rng = _rng(31)
+    T, E, k = 200, 8, 2
+    z = (rng.standard_normal((T, E)) * 2).astype(np.float32)
+    idx = O.select_topk(z, k)
+    counts = np.bincount(idx.ravel(), minlength=E)
+    st = O.routing_stats(z, counts, 7, k)
+    mask = Fnn.one_hot(torch.as_tensor(idx), num_classes=E).sum(dim=1).double()
+    freq = mask.mean(dim=0)
+    ratio = (torch.std(freq) / (torch.mean(freq) + 1e-8)).item()
+    assert abs(st["balance_ratio"] - ratio) < 1e-12
+    assert abs(st["l_balance"] - 0.01 * ratio) < 1e-14
+    assert abs(st["l_aux"] - 0.01 * (torch.std(freq).item() + 100 * freq.max().item())) < 1e-12
+    p = O.softmax(z)
+    ent = np.mean([sp_entropy(p[t]) for t in range(T)])
+    assert abs(st["entropy"] - ent) < 1e-12
+    np.testing.assert_allclose(st["utilization"].sum(), 1.0)
+    assert st["drop_rate"] == 7 / (T * k)
+    # uniform: ratio 0, l_aux = lambda*gamma*k/E; equal logits: entropy ln E
+    uni = O.routing_stats(np.zeros((16, 16), np.float32), np.full(16, 2), 0, 2)
+    assert uni["balance_ratio"] == 0.0
+    assert abs(uni["l_aux"] - 0.01 * 100 * 2 / 16) < 1e-15
+    assert abs(uni["entropy"] - math.log(16)) < 1e-12
+    np.testing.assert_allclose(uni["utilization"], 1 / 16)
+    # collapsed: one expert takes every token's first slot -> near-zero entropy when the
+    # logit gap is huge
+    zc = np.full((4, 4), -60.0, np.float32)
+    zc[:, 0] = 60.0
+    assert O.routing_stats(zc, np.array([4, 4, 0, 0]), 0, 2)["entropy"] < 1e-40
+
+
+
+
+PINS = [check_worked_combine, check_worked_layer, check_printed_gate, check_softmax_weights, check_ln3_weights,
         check_weight_formulations, check_topk_bruteforce, check_topk_margin,
         check_router_logits, check_capacity_rule, check_dispatch, check_activations,
-        check_expert_ffn, check_layer_special_cases, check_ledgers]
+        check_expert_ffn, check_layer_special_cases, check_ledgers, check_routing_stats]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -350,7 +428,7 @@ def _mut_highest_index_ties(z):
     return (E - 1 - np.argsort(-np.asarray(z, np.float64)[:, ::-1], axis=1, kind="stable"))
 
 
-def _mut_inverted_weights(z, idx):
+def _mut_inverted_weights(z, idx, mode="renormalized"):
     zs = np.take_along_axis(np.asarray(z, np.float64), idx, axis=1)
     e = np.exp(zs[:, :1] - zs)
     return e / e.sum(axis=1, keepdims=True)
@@ -390,8 +468,8 @@ def _mut_sigmoid_only(v):
     return 1.0 / (1.0 + np.exp(-np.asarray(v, np.float64)))
 
 
-def _mut_capacity_floor_no_k(T, k, E, factor=1.0):
-    return int(factor * T / E)
+def _mut_capacity_floor_no_k(T, k, E, factor=1.0, min_capacity=0):
+    return max(min_capacity, int(factor * T / E))
 
 
 def _mut_ledger_no_k(common, routed_total, E, k):
@@ -410,3 +488,19 @@ MUTATIONS = [("expert_order", _mut_highest_index_ties), ("topk_weights", _mut_in
 def test_mutation_is_caught(monkeypatch, name, bad):
     caught = _fails(monkeypatch, name, bad)
     assert caught, f"planted mistake in {name} ({bad.__name__}) passed every pin"
+
+
+def _mut_population_std(z, counts, n_dropped, k, lambda_balance=0.01, lambda_aux=0.01, gamma_aux=100.0):
+    r = _orig_stats(z, counts, n_dropped, k, lambda_balance, lambda_aux, gamma_aux)
+    u = np.asarray(counts, np.float64) / np.asarray(z).shape[0]
+    r["balance_ratio"] = float(np.std(u)) / float(np.mean(u))
+    return r
+
+
+_orig_stats = O.routing_stats
+
+
+def test_routing_stats_mutation_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "routing_stats", _mut_population_std)
+    with pytest.raises(AssertionError):
+        check_routing_stats()

@@ -41,6 +41,11 @@ SMALL = {
                                        dtype="bf16", shared=True),
     "bf16-capacity-one": MoEConfig("bf16-c1", 23, T=64, d=128, E=4, k=2, F=64, act="swiglu", dtype="bf16",
                                    capacity=1),
+    # routing weights = the selected softmax probabilities, not renormalised
+    "bf16-softmax-weights": MoEConfig("bf16-sw", 27, T=300, d=256, E=16, k=2, F=256, act="swiglu",
+                                      dtype="bf16", shared=True, bias_var=0.5, weights="softmax"),
+    "f32-softmax-weights-k1": MoEConfig("f32-sw", 28, T=129, d=64, E=8, k=1, F=128, act="gelu", dtype="f32",
+                                        weights="softmax"),
 }
 
 
@@ -200,6 +205,10 @@ def test_workload_full_size(num):
     inp = synth.make_inputs(cfg, DEV)
     torch.cuda.synchronize()
     res = run_layer(cfg, inp)
+    stats = B.routing_stats(torch.as_tensor(res["logits"], device=DEV),
+                            torch.as_tensor(res["counts"].astype(np.int32), device=DEV),
+                            torch.tensor([res["n_dropped"]], dtype=torch.int32, device=DEV), cfg.k)
+    sref = _check_stats(cfg, stats, res["logits"], res["counts"], res["n_dropped"], cfg.k)
     x64, wr64, b64 = _x64(inp)
     rep = {}
     z_o, flip = check_route(cfg, x64, wr64, b64, res, rep)
@@ -214,6 +223,37 @@ def test_workload_full_size(num):
     rep["n_dropped"] = res["n_dropped"]
     rep["drop_rate"] = res["n_dropped"] / (cfg.T * cfg.k)
     rep["load_min_max"] = (int(res["counts"].min()), int(res["counts"].max()))
+    rep["l_balance"], rep["l_aux"], rep["entropy"] = sref["l_balance"], sref["l_aux"], sref["entropy"]
     say(f"[ok] {cfg.name}: {rep}")
     del inp
     torch.cuda.empty_cache()
+
+
+def _check_stats(cfg, stats_gpu, logits, counts, n_dropped, k):
+    ref = O.routing_stats(logits, counts, n_dropped, k)
+    g = stats_gpu.cpu().numpy().astype(np.float64)
+    for i, name in enumerate(B.STAT_NAMES):
+        tol = 1e-5 if name == "entropy" else 1e-6
+        assert abs(g[i] - ref[name]) <= tol * max(1.0, abs(ref[name])), (name, g[i], ref[name])
+    np.testing.assert_allclose(g[5:], ref["utilization"], rtol=1e-6, atol=1e-9)
+    return ref
+
+
+@pytest.mark.parametrize("name", ["bf16-capacity", "bf16-shared-bias", "bf16-e384-top6-shared", "tiny-gelu-f32"])
+def test_routing_stats(name):
+    """Routing statistics through the layer and through moe_routing_stats, against the
+    oracle on the GPU's own logits and counts."""
+    cfg = SMALL[name]
+    inp = synth.make_inputs(cfg, DEV)
+    L = B.Layer(inp["w_r"], inp["w_gate"], inp["w_up"], inp["w_down"], cfg.k, act=cfg.act, bias=inp["bias"],
+                capacity=cfg.capacity, s_gate=inp["s_gate"], s_up=inp["s_up"], s_down=inp["s_down"], stats=True)
+    L(inp["x"])
+    torch.cuda.synchronize()
+    logits = L.logits.cpu().numpy()
+    counts = L.counts.cpu().numpy()
+    nd = int(L.n_dropped.item())
+    ref = _check_stats(cfg, L.stats, logits, counts, nd, cfg.k)
+    alone = B.routing_stats(L.logits, L.counts, L.n_dropped, cfg.k)
+    torch.cuda.synchronize()
+    assert torch.equal(alone, L.stats)                  # same kernels, same bits
+    say(f"[ok] stats {name}: {{{', '.join(f'{k}={v:.4g}' for k, v in ref.items() if k != 'utilization')}}}")
