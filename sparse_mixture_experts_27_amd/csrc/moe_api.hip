@@ -63,6 +63,16 @@ moe_status_t check_route_args(const void* x, const void* w_r, int dt, int64_t T,
   return MOE_OK;
 }
 
+// The bf16 kernels address each operand (x or H rows, one expert's weights) with 32-bit
+// byte offsets below 2^31.
+moe_status_t check_bf16_operands(int64_t max_rows, int64_t d, int64_t F) {
+  constexpr int64_t kMaxOperand = (int64_t{1} << 31) - 1;
+  if (max_rows * d * 2 > kMaxOperand || max_rows * F * 2 > kMaxOperand || F * d * 2 > kMaxOperand)
+    return fail(MOE_EUNSUPPORTED, "bf16 expert FFN operands must stay below 2 GiB (rows=%lld d=%lld F=%lld); "
+                "split the batch", (long long)max_rows, (long long)d, (long long)F);
+  return MOE_OK;
+}
+
 moe_status_t check_ffn_args(const void* x, const int32_t* offsets, int G, int64_t max_rows, int64_t d,
                             int64_t F, int act, int dt, const void* w_gate, const void* w_up,
                             const void* w_down, const void* y) {
@@ -74,6 +84,9 @@ moe_status_t check_ffn_args(const void* x, const int32_t* offsets, int G, int64_
   if (dt == MOE_BF16 && (d % 64 != 0 || F % 64 != 0))
     return fail(MOE_EUNSUPPORTED, "bf16 expert FFN needs d and F multiples of 64 (d=%lld F=%lld)",
                 (long long)d, (long long)F);
+  if (dt == MOE_BF16) {
+    if (moe_status_t st = check_bf16_operands(max_rows, d, F)) return st;
+  }
   if (!x || !offsets || !w_gate || !w_down || !y) return fail(MOE_EINVAL, "moe_expert_ffn: null required pointer");
   if (act == MOE_ACT_SWIGLU && !w_up) return fail(MOE_EINVAL, "SwiGLU needs w_up");
   if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_down) || (w_up && !aligned16(w_up)) || !aligned16(y))
@@ -256,6 +269,9 @@ moe_status_t moe_layer_forward(const moe_layer_args_t* a, hipStream_t stream) {
   for (const void* p : al)
     if (p && !aligned16(p)) return fail(MOE_EINVAL, "weights and out must be 16-byte aligned");
   if (a->T == 0) return MOE_OK;
+  if (a->dt == MOE_BF16) {
+    if (moe_status_t st = check_bf16_operands(a->T * a->k + (a->s_gate ? a->T : 0), a->d, a->F)) return st;
+  }
   const size_t need = moe_layer_workspace_bytes(a);
   if (!a->ws || a->ws_bytes < need)
     return fail(MOE_EWORKSPACE, "layer needs %zu workspace bytes, got %zu", need, a->ws_bytes);

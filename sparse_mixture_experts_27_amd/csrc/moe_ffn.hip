@@ -10,14 +10,15 @@
 // A device-side schedule (one tiny kernel) turns the group offsets into M-tiles, so
 // no host synchronisation is needed to learn how many rows each expert received.
 //
-// bf16 tile: 256 rows x 256 MFMA columns x 64 K per stage, 4 waves.  Wave w owns 64
-// columns of every row of the tile: its weight fragments are private to it and are
-// loaded straight from global memory into registers in the MFMA operand layout (no
-// LDS), while the activation tile is shared by the 4 waves through LDS (double-
-// buffered, 16-byte chunks XOR-swizzled by row).  Only the 16-row fragments that hold
-// real rows are multiplied, so a group with 70 rows costs 5 fragments, not 16.
-// Workgroups are remapped so that each XCD (blockIdx % 8) walks a contiguous range of
-// tiles: the tiles of one expert share its activation rows in that XCD's L2.
+// bf16 tile: up to 256 rows x 256 MFMA columns x 64 K per stage, 8 waves (2 per SIMD).
+// Wave w owns 32 columns of every row of the tile: its weight fragments are private to
+// it and are loaded straight from global memory into registers in the MFMA operand
+// layout (no LDS), while the activation tile is shared by the 8 waves through a ring of
+// 3 LDS slots, written by buffer-to-LDS loads (no register round trip), 16-byte chunks
+// XOR-swizzled by row.  Only the 16-row fragments that hold real rows are multiplied,
+// so a group with 70 rows costs 5 fragments, not 16.  Workgroups are remapped so that
+// each XCD (blockIdx % 8) walks a contiguous range of tiles: the tiles of one expert
+// share its activation rows in that XCD's L2.
 #include "moe_common.h"
 
 #include <cstdlib>
@@ -28,6 +29,7 @@ namespace {
 constexpr int BM = 256;          // rows per M-tile (bf16)
 constexpr int BK = 64;           // K per pipeline stage
 constexpr int BM_F32 = 64;       // rows per M-tile (fp32 path)
+constexpr int WEIGHT_RING = 3;   // weight register slots per wave (2 stages in flight)
 
 enum GemmMode { MODE_SWIGLU_UP = 0, MODE_GELU_UP = 1, MODE_DOWN = 2 };
 
@@ -156,6 +158,12 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& p, int bm, TileInfo&
   return true;
 }
 
+// Raw buffer resource over [base, base + 2^31): every offset the GEMM forms is below 2^31
+// (the host rejects larger operands), so the range check never triggers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), 0x7FFFFFFF, 0x00020000);
+}
+
 // Source row of the A operand for output row r of group g.
 __device__ __forceinline__ int64_t a_source_row(const GemmArgs& p, int mode, int g, int64_t r) {
   if (mode == MODE_DOWN) return r;
@@ -166,23 +174,29 @@ __device__ __forceinline__ int64_t a_source_row(const GemmArgs& p, int mode, int
 // Tile: MT*16 rows x 256 MFMA columns, K advanced BK=64 per pipeline stage, NW waves of
 // NF 16-column fragments each (NW * NF * 16 = 256).  With NW = 8 two waves share each
 // SIMD, so one wave's memory and LDS latency hides behind the other's MFMAs.
-// Weights: a ring of 3 register slots per wave (stage s is multiplied while s+1 and s+2
-// are in flight).  Activations: loaded one stage ahead into registers and stored into
-// a ring of 3 LDS slots.  Every global load is unconditional (padding rows read a valid
-// row of the tile and inactive waves read valid weight rows; neither result is stored)
-// so the compiler's memory counters stay exact, and activation loads are issued before
-// weight loads so that waiting for one stage's activations never waits for weights.
-// Per-lane addresses are 32-bit byte offsets from uniform base pointers.
+// Weights: a ring of WRING register slots per wave (stage s is multiplied while the next
+// WRING-1 stages are in flight).  Activations: buffer-to-LDS loads two stages ahead
+// into a ring of 3 LDS slots (when the tile has at least one 16-byte chunk per thread;
+// smaller tiles go through a 2-slot register ring and LDS stores).  Every global load
+// is unconditional (padding rows read a valid row of the tile and inactive waves read
+// valid weight rows; neither result is stored) so the memory counters stay in step
+// across waves, and activation loads are issued before weight loads so that waiting
+// for one stage's activations never waits for weights.  Loads are raw buffer loads:
+// uniform base, 32-bit per-lane offset, uniform stage offset.  The LDS slots arrive as
+// distinct restrict pointers so the compiler can tell a slot being read from the slots
+// being filled and does not wait for those loads before its LDS reads.
 template <int MODE, int MT, int NW>
-__global__ __launch_bounds__(NW * 64, 1) void ffn_gemm_bf16_kernel(GemmArgs p) {
+__device__ __forceinline__ void ffn_gemm_bf16_body(const GemmArgs& p, uint16_t* __restrict__ L0,
+                                                   uint16_t* __restrict__ L1, uint16_t* __restrict__ L2) {
   constexpr int NT = NW * 64;                     // threads
   constexpr int NF = 256 / (16 * NW);             // 16-column fragments per wave
   constexpr int WCOLS = NF * 16;                  // MFMA columns per wave
   constexpr int BMT = MT * 16;
   constexpr int AR = (BMT * 8 + NT - 1) / NT;     // 16-byte activation chunks per thread per stage
-  constexpr int RING = 3;
+  constexpr int LRING = 3;                        // LDS activation slots
+  constexpr int WRING = WEIGHT_RING;
   static_assert(NF >= 2 && NF * 16 * NW == 256, "tile shape");
-  __shared__ __attribute__((aligned(16))) uint16_t As[RING][BMT * BK];
+  auto lds = [&](int slot) -> uint16_t* { return slot == 0 ? L0 : slot == 1 ? L1 : L2; };
   TileInfo ti;
   if (!decode_tile(p, BMT, ti)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -227,42 +241,66 @@ __global__ __launch_bounds__(NW * 64, 1) void ffn_gemm_bf16_kernel(GemmArgs p) {
   for (int i = 0; i < AR; ++i) {
     const int r = WRAP ? ((i * NT + tid) >> 3) % BMT : (i * NT + tid) >> 3;
     const int rr = r < ti.nrows ? r : 0;    // padding rows repeat row 0 of the tile
+    const int cc = WRAP ? chunk : (chunk ^ (r & 7));
     aoff[i] = static_cast<uint32_t>((a_source_row(p, MODE, ti.g, ti.row_begin + rr) * p.K + k_begin +
-                                     chunk * 8) * 2);
+                                     cc * 8) * 2);
   }
+  // Buffer resources: uniform base + 32-bit per-lane offset + uniform stage offset.
+  const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(Ab);
+  const __amdgpu_buffer_rsrc_t w0rsrc = make_rsrc(Wb0);
+  const __amdgpu_buffer_rsrc_t w1rsrc = make_rsrc(Wb1);
   const int st_row0 = WRAP ? (tid >> 3) % BMT : (tid >> 3);
   const int st_off0 = st_row0 * BK + ((chunk ^ (st_row0 & 7)) * 8);   // element offset in a slot
 
   u32x4 ra[2][AR];                          // activation register ring: 2 stages
-  bf16x8 rb[RING][2][NF];                   // weight register ring: [slot][k32 step][fragment]
+  bf16x8 rb[WRING][2][NF];                  // weight register ring: [slot][k32 step][fragment]
 
   auto clamp_stage = [&](int st) { return st < 0 ? 0 : (st < nst ? st : nst - 1); };
-  auto load_a = [&](int st, int aslot) {
+  auto load_a = [&](int st, int aslot, int lslot) {
     st = clamp_stage(st);
-    const uint32_t ko = static_cast<uint32_t>(st) * (BK * 2);
+    const int ko = st * (BK * 2);           // uniform part of the offset
+    if (WRAP) {
 #pragma unroll
-    for (int i = 0; i < AR; ++i) ra[aslot][i] = *reinterpret_cast<const u32x4*>(Ab + (aoff[i] + ko));
+      for (int i = 0; i < AR; ++i) ra[aslot][i] = __builtin_amdgcn_raw_buffer_load_b128(arsrc, aoff[i], ko, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < AR; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc,
+            (__attribute__((address_space(3))) void*)(lds(lslot) + (i * (NT / 64) + wave) * 512), 16, aoff[i], ko, 0, 0);
+    }
   };
+  // Make the activations of a stage visible: with buffer-to-LDS loads, wait until this
+  // wave's loads of that stage have landed (the loads issued after them: 2 stages of
+  // weights, 2*NF each, and one stage of activations, AR) - the barrier that follows
+  // makes every wave's share visible.  Otherwise store the register copy into LDS.
   auto store_a = [&](int aslot, int lslot) {
+    if (!WRAP) {
+      constexpr int N = 4 * NF + AR;
+      static_assert(N < 64, "vmcnt range");
+      // s_waitcnt immediate (gfx9 layout): vmcnt in [3:0] and [15:14], expcnt [6:4] and
+      // lgkmcnt [11:8] left at their maxima (no wait)
+      __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < AR; ++i) {
       if (WRAP) {
         const int r = ((i * NT + tid) >> 3) % BMT;
-        *reinterpret_cast<u32x4*>(&As[lslot][r * BK + ((chunk ^ (r & 7)) * 8)]) = ra[aslot][i];
+        *reinterpret_cast<u32x4*>(&lds(lslot)[r * BK + ((chunk ^ (r & 7)) * 8)]) = ra[aslot][i];
       } else {
-        *reinterpret_cast<u32x4*>(&As[lslot][st_off0 + i * (NT / 8) * BK]) = ra[aslot][i];
+        *reinterpret_cast<u32x4*>(&lds(lslot)[st_off0 + i * (NT / 8) * BK]) = ra[aslot][i];
       }
     }
   };
   auto load_b = [&](int st, int slot) {
     st = clamp_stage(st);
-    const uint32_t ko = static_cast<uint32_t>(st) * (BK * 2);
+    const int ko = st * (BK * 2);           // uniform part of the offset
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int nf = 0; nf < NF; ++nf) {
-        const char* base = (MODE == MODE_SWIGLU_UP && nf >= NF / 2) ? Wb1 : Wb0;
-        rb[slot][s][nf] = *reinterpret_cast<const bf16x8*>(base + (boff[nf] + ko + s * 64));
+        const auto& rs = (MODE == MODE_SWIGLU_UP && nf >= NF / 2) ? w1rsrc : w0rsrc;
+        rb[slot][s][nf] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, boff[nf] + s * 64, ko, 0));
       }
   };
   // Mark a weight slot as consumed on every path (the MFMAs that read it sit behind the
@@ -276,7 +314,7 @@ __global__ __launch_bounds__(NW * 64, 1) void ffn_gemm_bf16_kernel(GemmArgs p) {
   auto read_a = [&](int slot, int s, int mf) {
     const int r = mf * 16 + (lane & 15);
     const int c = (s * 4 + (lane >> 4)) ^ (r & 7);
-    return *reinterpret_cast<const bf16x8*>(&As[slot][r * BK + c * 8]);
+    return *reinterpret_cast<const bf16x8*>(&lds(slot)[r * BK + c * 8]);
   };
 
   f32x4 acc[MT][NF];
@@ -324,29 +362,51 @@ __global__ __launch_bounds__(NW * 64, 1) void ffn_gemm_bf16_kernel(GemmArgs p) {
     }
   };
 
-  // Pipeline.  In the phase of stage st: load activations and weights of stage st+2
-  // (activations first), multiply stage st, store the activations of stage st+1 into LDS,
-  // barrier.  The memory counter is in issue order, so the wait before that store only
-  // covers loads issued up to the previous phase: the weights of stages st+1 and st+2 stay
-  // in flight across it.  Weights use 3 register slots (stage mod 3), activations 2
-  // register slots (stage mod 2) and 3 LDS slots (stage mod 3).  The pipeline starts at
-  // stage -2 so every load is issued inside the loop and the loop-carried memory waits
-  // are exact; base = -2 = 4 (mod 6) keeps every slot index a compile-time constant.
+  // Pipeline.  In the phase of stage st: start the activations of stage st+2 and the
+  // weights of stage st+WRING-1 (activations first), multiply stage st, make the
+  // activations of stage st+1 visible in LDS, barrier.  The memory counter is in issue
+  // order, so the wait for stage st+1's activations only covers loads issued up to the
+  // previous phase: later weights stay in flight across it.  Stage s uses weight register
+  // slot s mod WRING, activation register slot s mod 2 and LDS slot s mod 3.  The phases
+  // of the negative stages (loads only) are peeled, so every load is issued inside the
+  // pipeline and the steady-state loop has one path: its memory waits are exact.  The
+  // loop is unrolled U times (a multiple of every ring length) and leaves through a jump,
+  // so every slot index is a compile-time constant and the loop header merges one state.
+  constexpr int B0 = 1 - WRING;
+  constexpr int U = WRING % 6 == 0 ? WRING : WRING % 3 == 0 ? 2 * WRING : WRING % 2 == 0 ? 3 * WRING : 6 * WRING;
+  static_assert(U % WRING == 0 && U % 2 == 0 && U % 3 == 0, "unroll");
+  auto pm = [](int a, int m) { return ((a % m) + m) % m; };
+  auto barrier = [&]() {
+    if (WRAP) {
+      __syncthreads();
+    } else {              // the activations' LDS writes were waited for by store_a
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
+  };
   if (nst > 0) {
-    for (int base = -2; base < nst; base += 6) {
 #pragma unroll
-      for (int ph = 0; ph < 6; ++ph) {
+    for (int st = B0; st < 0; ++st) {
+      load_a(st + 2, pm(st + 2, 2), pm(st + 2, LRING));
+      load_b(st + WRING - 1, pm(st + WRING - 1, WRING));
+      if (st + 1 >= 0) store_a(pm(st + 1, 2), pm(st + 1, LRING));
+      barrier();
+    }
+    for (int base = 0;; base += U) {
+#pragma unroll
+      for (int ph = 0; ph < U; ++ph) {
         const int st = base + ph;
-        if (st >= nst) break;
-        load_a(st + 2, ph % 2);
-        load_b(st + 2, ph % 3);
-        if (st >= 0) compute((ph + 1) % 3, (ph + 1) % 3);
-        consume_b((ph + 1) % 3);
-        if (st + 1 >= 0) store_a((ph + 1) % 2, (ph + 2) % 3);
-        __syncthreads();
+        if (st >= nst) goto pipeline_done;
+        load_a(st + 2, pm(ph + 2, 2), pm(ph + 2, LRING));
+        load_b(st + WRING - 1, pm(ph + WRING - 1, WRING));
+        compute(pm(ph, LRING), pm(ph, WRING));
+        consume_b(pm(ph, WRING));
+        store_a(pm(ph + 1, 2), pm(ph + 1, LRING));
+        barrier();
       }
     }
   }
+pipeline_done:
 
   // ---- epilogue.  C layout: lane holds rows 4*(lane/16)+v of each 16x16 block, column lane%16.
   if (!wave_on) return;
@@ -385,6 +445,14 @@ __global__ __launch_bounds__(NW * 64, 1) void ffn_gemm_bf16_kernel(GemmArgs p) {
       }
     }
   }
+}
+
+template <int MODE, int MT, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void ffn_gemm_bf16_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint16_t As0[MT * 16 * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t As1[MT * 16 * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t As2[MT * 16 * BK];
+  ffn_gemm_bf16_body<MODE, MT, NW>(p, As0, As1, As2);
 }
 
 // ---- fp32 path: 64 x 64 output tile, 256 threads x (4 x 4), K staged 16 at a time.

@@ -102,6 +102,10 @@ def test_ffn_validation(lib):
     assert lib.moe_expert_ffn(*small) == 3
     bad_act = list(base); bad_act[8] = 5
     assert lib.moe_expert_ffn(*bad_act) == 1
+    huge = list(base); huge[5] = 80000               # H = 80000 x 14336 bf16 rows > 2 GiB
+    huge[15] = lib.moe_expert_ffn_workspace_bytes(80000, 64, 4096, 14336, B.MOE_ACT_SWIGLU, B.MOE_BF16)
+    assert lib.moe_expert_ffn(*huge) == 2
+    assert b"2 GiB" in lib.moe_last_error()
 
 
 def test_combine_validation(lib):
