@@ -195,7 +195,10 @@ __device__ __forceinline__ void ffn_gemm_bf16_body(const GemmArgs& p, uint16_t* 
   constexpr int AR = (BMT * 8 + NT - 1) / NT;     // 16-byte activation chunks per thread per stage
   constexpr int LRING = 3;                        // LDS activation slots
   constexpr int WRING = WEIGHT_RING;
-  static_assert(NF >= 2 && NF * 16 * NW == 256, "tile shape");
+  // With one fragment per wave (16 waves), a SwiGLU wave's 16 columns pair 8 gate rows
+  // (lanes with lane%16 < 8) with the 8 up rows of the same hidden units (lane%16 >= 8).
+  constexpr bool PAIRED = MODE == MODE_SWIGLU_UP && NF == 1;
+  static_assert(NF >= 1 && NF * 16 * NW == 256, "tile shape");
   auto lds = [&](int slot) -> uint16_t* { return slot == 0 ? L0 : slot == 1 ? L1 : L2; };
   TileInfo ti;
   if (!decode_tile(p, BMT, ti)) return;
@@ -218,17 +221,20 @@ __device__ __forceinline__ void ffn_gemm_bf16_body(const GemmArgs& p, uint16_t* 
   const char* Wb1 = reinterpret_cast<const char*>(static_cast<const uint16_t*>(shared_grp ? p.sw1 : p.w1) + wstride);
   if (MODE != MODE_SWIGLU_UP) Wb1 = Wb0;
   int64_t col_base;                         // first output column of this wave
-  if (MODE == MODE_SWIGLU_UP) col_base = static_cast<int64_t>(ti.ntile) * 128 + wave * (WCOLS / 2);
+  if (MODE == MODE_SWIGLU_UP) col_base = static_cast<int64_t>(ti.ntile) * 128 + wave * (WCOLS / 2);   // hidden unit
   else col_base = static_cast<int64_t>(ti.ntile) * 256 + wave * WCOLS;
   const bool wave_on = col_base < p.N;
   uint32_t boff[NF];                        // byte offsets of this lane's weight rows
 #pragma unroll
   for (int nf = 0; nf < NF; ++nf) {
-    int64_t wrow = (MODE == MODE_SWIGLU_UP) ? col_base + (nf % (NF / 2)) * 16 + (lane & 15)
+    int64_t wrow = PAIRED ? col_base + (lane & 7)
+                 : (MODE == MODE_SWIGLU_UP) ? col_base + (nf % (NF / 2)) * 16 + (lane & 15)
                                             : col_base + nf * 16 + (lane & 15);
     if (!wave_on) wrow = lane & 15;         // a valid row; the result is not stored
     boff[nf] = static_cast<uint32_t>((wrow * p.K + k_begin + 8 * (lane >> 4)) * 2);
   }
+  // paired layout: this lane's weight row lives in the gate or the up tensor
+  const char* wlane = PAIRED ? ((lane & 8) ? Wb1 : Wb0) + boff[0] : nullptr;
 
   // ---- activation chunks loaded by this thread: chunk q = i*NT + tid -> row q/8 (mod
   // the tile height; a repeated row writes identical bytes), 16-byte column q%8 = tid%8.
@@ -295,6 +301,11 @@ __device__ __forceinline__ void ffn_gemm_bf16_body(const GemmArgs& p, uint16_t* 
   auto load_b = [&](int st, int slot) {
     st = clamp_stage(st);
     const int ko = st * (BK * 2);           // uniform part of the offset
+    if (PAIRED) {                           // per-lane tensor: a 64-bit address
+#pragma unroll
+      for (int s = 0; s < 2; ++s) rb[slot][s][0] = *reinterpret_cast<const bf16x8*>(wlane + ko + s * 64);
+      return;
+    }
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -416,6 +427,13 @@ pipeline_done:
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int r = mf * 16 + 4 * (lane >> 4) + v;
+        if (PAIRED) {                       // lanes 8..15 of each row group hold the up half
+          const float g = acc[mf][0][v];
+          const float u = __shfl_xor(g, 8);
+          if (r < ti.nrows && (lane & 8) == 0)
+            static_cast<uint16_t*>(p.out)[(ti.row_begin + r) * p.N + col_base + (lane & 7)] = f32_to_bf16(silu_f(g) * u);
+          continue;
+        }
         if (r < ti.nrows) {
           const int64_t orow = ti.row_begin + r;
           if (MODE == MODE_SWIGLU_UP) {
@@ -546,7 +564,14 @@ __global__ __launch_bounds__(256) void ffn_reduce_splits_kernel(const float* __r
 template <int MODE>
 void launch_bf16_gemm(int bm, int nw, int64_t grid, const GemmArgs& g, hipStream_t s) {
   const unsigned gr = static_cast<unsigned>(grid);
-  if (nw == 8) {
+  if (nw == 16) {
+    switch (bm) {
+      case 32: ffn_gemm_bf16_kernel<MODE, 2, 16><<<gr, 1024, 0, s>>>(g); break;
+      case 64: ffn_gemm_bf16_kernel<MODE, 4, 16><<<gr, 1024, 0, s>>>(g); break;
+      case 128: ffn_gemm_bf16_kernel<MODE, 8, 16><<<gr, 1024, 0, s>>>(g); break;
+      default: ffn_gemm_bf16_kernel<MODE, 16, 16><<<gr, 1024, 0, s>>>(g); break;
+    }
+  } else if (nw == 8) {
     switch (bm) {
       case 32: ffn_gemm_bf16_kernel<MODE, 2, 8><<<gr, 512, 0, s>>>(g); break;
       case 64: ffn_gemm_bf16_kernel<MODE, 4, 8><<<gr, 512, 0, s>>>(g); break;
@@ -586,7 +611,7 @@ FfnPlan ffn_plan(int64_t max_rows, int G, bool has_shared, int64_t d, int64_t F,
       if (v == 32 || v == 64 || v == 128 || v == 256) pl.bm = v;
     }
     pl.nw = 8;
-    if (const char* o = getenv("MOE_TILE_WAVES")) pl.nw = atoi(o) == 4 ? 4 : 8;
+    if (const char* o = getenv("MOE_TILE_WAVES")) pl.nw = atoi(o) == 4 ? 4 : atoi(o) == 16 ? 16 : 8;
   } else {
     pl.bm = BM_F32;
   }

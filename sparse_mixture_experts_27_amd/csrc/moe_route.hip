@@ -3,9 +3,13 @@
 // §3.3 (w_i = p_i / (p_i + p_j)); [200B-5] "谁来决定请哪几个专家？" (top-k).
 //
 // One workgroup (4 waves) owns 16 tokens.  bf16: the router GEMM runs on
-// v_mfma_f32_16x16x32_bf16 with W_r staged through LDS transposed to [expert][k];
-// each wave takes a quarter of every 256-wide K chunk and the four partial sums are
-// added in a fixed order, so the logits are bit-reproducible.  fp32: plain FMA.
+// v_mfma_f32_16x16x32_bf16.  When d is a multiple of 32, a small pass first writes
+// W_r transposed to [expert][k] (16 experts padded with zeros) into the workspace, and
+// every wave then loads both operands straight from memory in the MFMA layout, wave w
+// taking the 32-wide K steps w, w+4, w+8, ...; otherwise W_r is staged through LDS
+// transposed, each wave taking a quarter of every 256-wide K chunk.  Either way the
+// four partial sums are added in a fixed order, so the logits are bit-reproducible.
+// fp32: plain FMA.
 // The top-k epilogue runs one wave per token on a 64-bit key (ordered logit, inverted
 // expert index): the largest key is the largest logit, ties going to the lowest index.
 #include "moe_common.h"
@@ -213,6 +217,98 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
   finish_tokens(sm, tok0, T, E, k, mode, topk_idx, topk_w);
 }
 
+// W_r [d, E] -> wt [Ep, d] (Ep = E rounded up to 16, padding rows zero), 64 x 64 tiles.
+__global__ __launch_bounds__(256) void route_transpose_kernel(const uint16_t* __restrict__ w_r, int64_t d, int E,
+                                                              int Ep, uint16_t* __restrict__ wt) {
+  __shared__ uint16_t tile[64][65];
+  const int64_t k0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int e0 = blockIdx.y * 64;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int kk = i / 64, ee = i % 64;              // read along e (contiguous in W_r)
+    const int64_t k = k0 + kk;
+    const int e = e0 + ee;
+    tile[kk][ee] = (k < d && e < E) ? w_r[k * E + e] : 0;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int ee = i / 64, kk = i % 64;              // write along k (contiguous in wt)
+    const int64_t k = k0 + kk;
+    const int e = e0 + ee;
+    if (k < d && e < Ep) wt[static_cast<int64_t>(e) * d + k] = tile[kk][ee];
+  }
+}
+
+// Router GEMM with both operands loaded from memory in the MFMA layout (d % 32 == 0):
+// A = 16 token rows of x, B = 16-expert row blocks of wt [Ep, d].  blockIdx.y selects a
+// K range as in route_bf16_kernel; within it wave w takes the K steps w, w+4, ...
+__global__ __launch_bounds__(256) void route_mfma_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wt, const float* __restrict__ bias,
+    int64_t T, int64_t d, int E, int Ep, int k, int mode, int64_t kchunk, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, float* __restrict__ logits, float* __restrict__ partial) {
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  RouteSmem sm(smem_raw, E, true);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * RT_TOK;
+  const bool split = gridDim.y > 1;
+  const int64_t kb = static_cast<int64_t>(blockIdx.y) * kchunk;
+  const int64_t ke = kb + kchunk < d ? kb + kchunk : d;
+  const int nsteps = ke > kb ? static_cast<int>((ke - kb) / 32) : 0;
+  const int64_t my_tok = tok0 + (lane & 15);
+  const uint16_t* xrow = x + (my_tok < T ? my_tok : 0) * d + kb + 8 * (lane >> 4);   // rows past T: ignored
+  constexpr int U = 4;                       // K steps in flight per wave
+
+  for (int e0 = 0; e0 < Ep; e0 += RT_EB) {
+    const int nfr = (Ep - e0) / 16 < 4 ? (Ep - e0) / 16 : 4;   // 16-expert blocks in this pass
+    const uint16_t* wrow = wt + static_cast<int64_t>(e0 + (lane & 15)) * d + kb + 8 * (lane >> 4);
+    f32x4 acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j0 = wave; j0 < nsteps; j0 += 4 * U) {
+      bf16x8 a[U], b[U][4];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = j0 + 4 * u < nsteps ? j0 + 4 * u : j0;    // past the range: a repeated step, not used
+        a[u] = *reinterpret_cast<const bf16x8*>(xrow + j * 32);
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf)
+          b[u][nf] = *reinterpret_cast<const bf16x8*>(wrow + static_cast<int64_t>(nf < nfr ? nf : 0) * 16 * d + j * 32);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (j0 + 4 * u < nsteps) {
+#pragma unroll
+          for (int nf = 0; nf < 4; ++nf)
+            if (nf < nfr) acc[nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u][nf], acc[nf], 0, 0, 0);
+        }
+      }
+    }
+    // C layout of the 16x16 MFMA: lane holds rows 4*(lane/16)+v, column lane%16
+    __syncthreads();                         // previous pass's partials consumed
+#pragma unroll
+    for (int nf = 0; nf < 4; ++nf)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sm.red[wave][4 * (lane >> 4) + v][nf * 16 + (lane & 15)] = acc[nf][v];
+    __syncthreads();
+    for (int i = tid; i < RT_TOK * RT_EB; i += 256) {
+      const int t = i / RT_EB, e = e0 + i % RT_EB;
+      if (e < E) {
+        float z = ((sm.red[0][t][i % RT_EB] + sm.red[1][t][i % RT_EB]) + sm.red[2][t][i % RT_EB]) +
+                  sm.red[3][t][i % RT_EB];
+        if (split) {
+          if (tok0 + t < T) partial[(static_cast<int64_t>(blockIdx.y) * T + tok0 + t) * E + e] = z;
+        } else {
+          if (bias) z += bias[e];
+          sm.z[t * E + e] = z;
+          if (tok0 + t < T) logits[(tok0 + t) * E + e] = z;
+        }
+      }
+    }
+  }
+  if (split) return;
+  __syncthreads();
+  finish_tokens(sm, tok0, T, E, k, mode, topk_idx, topk_w);
+}
+
 // Sum the K-range partial logits in range order, add the offsets, finish the tokens.
 __global__ __launch_bounds__(256) void route_finish_kernel(const float* __restrict__ partial, int nsplit,
                                                            const float* __restrict__ bias, int64_t T, int E,
@@ -271,9 +367,17 @@ int route_splits(int64_t T, int64_t d, int dt) {
   return ks;
 }
 
+// The transposed-operand router needs d % 32 == 0 (whole 32-wide K steps in every range).
+bool route_direct(int64_t d, int dt) { return dt == MOE_BF16 && d % 32 == 0; }
+int route_padded_experts(int E) { return (E + 15) / 16 * 16; }
+
+size_t route_wt_bytes(int64_t d, int E, int dt) {
+  return route_direct(d, dt) ? align_up(static_cast<size_t>(route_padded_experts(E)) * d * sizeof(uint16_t), 256) : 0;
+}
+
 size_t route_ws_bytes(int64_t T, int64_t d, int E, int dt) {
   const int ks = route_splits(T, d, dt);
-  return ks > 1 ? static_cast<size_t>(ks) * T * E * sizeof(float) : 0;
+  return route_wt_bytes(d, E, dt) + (ks > 1 ? static_cast<size_t>(ks) * T * E * sizeof(float) : 0);
 }
 
 moe_status_t launch_route(const void* x, const void* w_r, const float* bias, int dt, int64_t T,
@@ -286,16 +390,28 @@ moe_status_t launch_route(const void* x, const void* w_r, const float* bias, int
     const int64_t chunks = (d + RT_KC - 1) / RT_KC;
     const int64_t kchunk = ((chunks + ks - 1) / ks) * RT_KC;
     const size_t smem = route_smem_bytes(E, true);
-    set_max_dynamic_smem(reinterpret_cast<const void*>(route_bf16_kernel), smem);
-    route_bf16_kernel<<<dim3(grid, ks), 256, smem, s>>>(static_cast<const uint16_t*>(x),
-                                                        static_cast<const uint16_t*>(w_r), bias, T, d, E, k,
-                                                        mode, kchunk, topk_idx, topk_w, logits, static_cast<float*>(ws));
+    const size_t wtb = route_wt_bytes(d, E, dt);
+    float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + wtb);
+    if (route_direct(d, dt)) {
+      const int Ep = route_padded_experts(E);
+      uint16_t* wt = static_cast<uint16_t*>(ws);
+      route_transpose_kernel<<<dim3(static_cast<unsigned>((d + 63) / 64), static_cast<unsigned>((Ep + 63) / 64)), 256,
+                               0, s>>>(static_cast<const uint16_t*>(w_r), d, E, Ep, wt);
+      if (moe_status_t st = check_launch("route transpose kernel")) return st;
+      set_max_dynamic_smem(reinterpret_cast<const void*>(route_mfma_kernel), smem);
+      route_mfma_kernel<<<dim3(grid, ks), 256, smem, s>>>(static_cast<const uint16_t*>(x), wt, bias, T, d, E, Ep, k,
+                                                          mode, kchunk, topk_idx, topk_w, logits, partial);
+    } else {
+      set_max_dynamic_smem(reinterpret_cast<const void*>(route_bf16_kernel), smem);
+      route_bf16_kernel<<<dim3(grid, ks), 256, smem, s>>>(static_cast<const uint16_t*>(x),
+                                                          static_cast<const uint16_t*>(w_r), bias, T, d, E, k,
+                                                          mode, kchunk, topk_idx, topk_w, logits, partial);
+    }
     if (moe_status_t st = check_launch("route kernel")) return st;
     if (ks > 1) {
       const size_t smem2 = route_smem_bytes(E, false);
       set_max_dynamic_smem(reinterpret_cast<const void*>(route_finish_kernel), smem2);
-      route_finish_kernel<<<grid, 256, smem2, s>>>(static_cast<const float*>(ws), ks, bias, T, E, k, mode, topk_idx,
-                                                   topk_w, logits);
+      route_finish_kernel<<<grid, 256, smem2, s>>>(partial, ks, bias, T, E, k, mode, topk_idx, topk_w, logits);
       return check_launch("route finish kernel");
     }
     return MOE_OK;

@@ -69,10 +69,14 @@ def test_route_validation(lib):
     assert _route(lib, mode=2) == 1          # unknown weights mode
     assert _route(lib, T=0) == 0             # no-op, nothing launched
     assert lib.moe_last_error() == b""
-    # few tokens split the contraction over workgroups: partial logits need a workspace
+    # bf16 with d % 32 == 0: W_r transposed to [expert][k] (experts padded to 16) ...
+    wt = 64 * 4096 * 2
+    assert lib.moe_route_workspace_bytes(4096, 4096, 64, B.MOE_BF16) == wt
+    assert lib.moe_route_workspace_bytes(4096, 4096, 60, B.MOE_BF16) == wt
+    # ... and few tokens split the contraction over workgroups: partial logits too
     need = lib.moe_route_workspace_bytes(16, 4096, 64, B.MOE_BF16)
-    assert need == 16 * 16 * 64 * 4
-    assert lib.moe_route_workspace_bytes(4096, 4096, 64, B.MOE_BF16) == 0
+    assert need == wt + 16 * 16 * 64 * 4
+    assert lib.moe_route_workspace_bytes(4096, 4004, 64, B.MOE_BF16) == 0   # d % 32 != 0: LDS-staged path
     assert lib.moe_route_workspace_bytes(16, 4096, 64, B.MOE_F32) == 0
     assert _route(lib, T=16, d=4096, E=64, ws=16, ws_bytes=need - 1) == 3
 

@@ -127,6 +127,25 @@ def test_worked_example_on_gpu():
     np.testing.assert_allclose(out.cpu().numpy()[0], g["mixture"], atol=1e-5)
 
 
+@pytest.mark.parametrize("T,d,E,k", [(37, 200, 12, 3), (600, 200, 40, 2), (600, 224, 12, 2), (5, 4096, 70, 4),
+                                     (300, 512, 130, 6)])
+def test_route_shapes(T, d, E, k):
+    """moe_route alone on shapes the layers above do not reach: d not a multiple of 32
+    (W_r staged through LDS), E not a multiple of 16 (padded expert blocks), more than
+    64 experts (several expert passes), few tokens (split contraction)."""
+    cfg = MoEConfig("route", 30 + T % 7 + d % 5, T=T, d=d, E=E, k=k, F=64, act="swiglu", dtype="bf16",
+                    bias_var=0.5)
+    say(f"[case] route {cfg.label}")
+    inp = synth.make_inputs(cfg, DEV)
+    idx, w, logits = B.route(inp["x"], inp["w_r"], k, bias=inp["bias"])
+    torch.cuda.synchronize()
+    res = dict(idx=idx.cpu().numpy().astype(np.int64), w=w.cpu().numpy().astype(np.float64),
+               logits=logits.cpu().numpy())
+    rep = {}
+    check_route(cfg, *_x64(inp), res, rep)
+    say(f"[ok] route {cfg.name}: {rep}")
+
+
 def test_stage_entry_points():
     """The four stage calls used one by one, each against the oracle."""
     cfg = MoEConfig("stages", 26, T=300, d=256, E=8, k=2, F=320, act="swiglu", dtype="bf16",
