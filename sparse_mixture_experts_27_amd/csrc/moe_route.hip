@@ -10,8 +10,9 @@
 // transposed, each wave taking a quarter of every 256-wide K chunk.  Either way the
 // four partial sums are added in a fixed order, so the logits are bit-reproducible.
 // fp32: plain FMA.
-// The top-k epilogue runs one wave per token on a 64-bit key (ordered logit, inverted
-// expert index): the largest key is the largest logit, ties going to the lowest index.
+// The top-k epilogue runs one 16-lane row per token (the workgroup's 16 tokens at once)
+// on a 64-bit key (ordered logit, inverted expert index): the largest key is the largest
+// logit, ties going to the lowest index; row maxima and sums use DPP lane moves.
 #include "moe_common.h"
 
 namespace moe {
@@ -27,7 +28,7 @@ struct RouteSmem {
   uint16_t (*wt)[RT_PITCH];   // [RT_EB][RT_PITCH]  W_r chunk, [expert][k]   (bf16 path)
   float (*red)[RT_TOK][RT_EB];// [4][RT_TOK][RT_EB] per-wave partial logits (bf16 path)
   float* z;                   // [RT_TOK][E]        final logits of the 16 tokens
-  float* zs;                  // [4][E]             selected logits, one row per wave
+  float* zs;                  // [RT_TOK][E]        selected logits, one row per token
   __device__ RouteSmem(char* base, int E, bool gemm) {
     size_t off = 0;
     if (gemm) {
@@ -43,7 +44,7 @@ struct RouteSmem {
 };
 
 inline size_t route_smem_bytes(int E, bool gemm) {
-  size_t b = sizeof(float) * (RT_TOK + 4) * static_cast<size_t>(E);
+  size_t b = sizeof(float) * (2 * RT_TOK) * static_cast<size_t>(E);
   if (gemm) b += sizeof(uint16_t) * RT_EB * RT_PITCH + sizeof(float) * 4 * RT_TOK * RT_EB;
   return b;
 }
@@ -65,62 +66,84 @@ __device__ __forceinline__ float key_to_float(uint32_t o) {
   return __uint_as_float(b);
 }
 
-// Top-k of one token's logits zrow[0..E) by one wave; writes idx/w rows.  zs is this
-// wave's LDS row for the selected logits.
-__device__ void topk_one_token(const float* zrow, float* zs, int E, int k, int mode, int32_t* idx_out,
-                               float* w_out) {
-  const int lane = threadIdx.x & 63;
-  const int per_lane = (E + 63) / 64;      // <= 16
-  uint32_t removed = 0;
+// Cross-lane steps inside 16-lane rows with DPP (VALU moves, no LDS round trip).
+// Controls: quad_perm [1,0,3,2] = 0xB1, quad_perm [2,3,0,1] = 0x4E, row_ror:4 = 0x124,
+// row_ror:8 = 0x128.  After the four steps every lane of a row has combined all 16.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+template <int CTRL>
+__device__ __forceinline__ void key_max_step(uint32_t& hi, uint32_t& lo) {
+  const uint32_t ohi = dpp_u32<CTRL>(hi), olo = dpp_u32<CTRL>(lo);
+  if (ohi > hi || (ohi == hi && olo > lo)) { hi = ohi; lo = olo; }
+}
+__device__ __forceinline__ void row16_key_max(uint32_t& hi, uint32_t& lo) {
+  key_max_step<0xB1>(hi, lo);
+  key_max_step<0x4E>(hi, lo);
+  key_max_step<0x124>(hi, lo);
+  key_max_step<0x128>(hi, lo);
+}
+// Sum over a 16-lane row in a fixed pattern (the same in every row and every call).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x124>(v);
+  v += dpp_f32<0x128>(v);
+  return v;
+}
+
+// Top-k of one token's logits zrow[0..E) by the 16 lanes of one DPP row (sl = lane % 16
+// holds experts sl, sl+16, ...); writes the idx/w rows.  zs: this token's LDS row for the
+// selected logits.  Keys are 64-bit (ordered logit, inverted expert index): the largest
+// key is the largest logit, ties going to the lowest index.
+__device__ void topk_row16(const float* zrow, float* zs, int E, int k, int mode, int32_t* idx_out, float* w_out) {
+  const int sl = threadIdx.x & 15;
+  const int per_lane = (E + 15) / 16;      // <= 64
+  uint64_t removed = 0;
+  float z0 = 0.f;
   for (int j = 0; j < k; ++j) {
-    // best remaining candidate of this lane
-    uint32_t bhi = 0, blo = 0;
+    uint32_t bhi = 0, blo = 0;             // best remaining candidate of this lane
     for (int i = 0; i < per_lane; ++i) {
-      const int e = lane + 64 * i;
+      const int e = sl + 16 * i;
       if (e < E && !((removed >> i) & 1u)) {
         const uint32_t hi = ordered_key(zrow[e]);
         const uint32_t lo = 0xffffffffu - static_cast<uint32_t>(e);
         if (hi > bhi || (hi == bhi && lo > blo)) { bhi = hi; blo = lo; }
       }
     }
-    // wave-wide max of the 64-bit key (hi, lo)
-    uint32_t mhi = bhi, mlo = blo;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const uint32_t ohi = __shfl_xor(mhi, off);
-      const uint32_t olo = __shfl_xor(mlo, off);
-      if (ohi > mhi || (ohi == mhi && olo > mlo)) { mhi = ohi; mlo = olo; }
-    }
-    const int e_win = static_cast<int>(0xffffffffu - mlo);
-    if ((e_win & 63) == lane) removed |= 1u << (e_win >> 6);
-    if (lane == 0) { idx_out[j] = e_win; zs[j] = key_to_float(mhi); }
+    row16_key_max(bhi, blo);
+    const int e_win = static_cast<int>(0xffffffffu - blo);
+    if ((e_win & 15) == sl) removed |= uint64_t{1} << (e_win >> 4);
+    const float zw = key_to_float(bhi);
+    if (j == 0) z0 = zw;
+    if (sl == 0) { idx_out[j] = e_win; zs[j] = zw; }
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   // renormalised: w_j = exp(z_j - z_0) / sum_{i<k} exp(z_i - z_0)
   // softmax mode:  w_j = exp(z_j - z_0) / sum_{all e} exp(z_e - z_0)   (z_0 is the max)
-  // fixed butterfly order in both
-  const float z0 = zs[0];
   float part = 0.f;
   if (mode == MOE_WEIGHTS_SOFTMAX) {
-    for (int e = lane; e < E; e += 64) part += expf(zrow[e] - z0);
+    for (int e = sl; e < E; e += 16) part += expf(zrow[e] - z0);
   } else {
-    for (int j = lane; j < k; j += 64) part += expf(zs[j] - z0);
+    for (int j = sl; j < k; j += 16) part += expf(zs[j] - z0);
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-  const float inv = 1.0f / part;
-  for (int j = lane; j < k; j += 64) w_out[j] = expf(zs[j] - z0) * inv;
+  const float inv = 1.0f / row16_sum(part);
+  for (int j = sl; j < k; j += 16) w_out[j] = expf(zs[j] - z0) * inv;
   __builtin_amdgcn_wave_barrier();
 }
 
+// The workgroup's 16 tokens, one per 16-lane row (wave w: tokens 4w..4w+3).
 __device__ void finish_tokens(RouteSmem& sm, int64_t tok0, int64_t T, int E, int k, int mode,
                               int32_t* topk_idx, float* topk_w) {
-  const int wave = threadIdx.x >> 6;
-  for (int t = wave; t < RT_TOK; t += 4) {
-    const int64_t tok = tok0 + t;
-    if (tok < T) topk_one_token(sm.z + t * E, sm.zs + wave * E, E, k, mode, topk_idx + tok * k, topk_w + tok * k);
-  }
+  const int t = threadIdx.x >> 4;
+  const int64_t tok = tok0 + t;
+  if (tok < T) topk_row16(sm.z + t * E, sm.zs + t * k, E, k, mode, topk_idx + tok * k, topk_w + tok * k);
 }
 
 // blockIdx.y selects a K range [ky*kchunk, (ky+1)*kchunk).  With one range the kernel
@@ -217,24 +240,38 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
   finish_tokens(sm, tok0, T, E, k, mode, topk_idx, topk_w);
 }
 
-// W_r [d, E] -> wt [Ep, d] (Ep = E rounded up to 16, padding rows zero), 64 x 64 tiles.
+// W_r [d, E] -> wt [Ep, d] (Ep = E rounded up to 16, padding rows zero); 32 k x 64 e
+// tiles, 4-byte accesses on both sides.  d % 32 == 0 here; E may be odd.
 __global__ __launch_bounds__(256) void route_transpose_kernel(const uint16_t* __restrict__ w_r, int64_t d, int E,
                                                               int Ep, uint16_t* __restrict__ wt) {
-  __shared__ uint16_t tile[64][65];
-  const int64_t k0 = static_cast<int64_t>(blockIdx.x) * 64;
+  __shared__ uint16_t tile[32][66];
+  const int64_t k0 = static_cast<int64_t>(blockIdx.x) * 32;
   const int e0 = blockIdx.y * 64;
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int kk = i / 64, ee = i % 64;              // read along e (contiguous in W_r)
-    const int64_t k = k0 + kk;
-    const int e = e0 + ee;
-    tile[kk][ee] = (k < d && e < E) ? w_r[k * E + e] : 0;
+  const int t = threadIdx.x;
+  {                                                  // read: row kk, experts 2q, 2q+1
+    const int kk = t >> 3, q0 = (t & 7) * 4;
+    const uint16_t* row = w_r + (k0 + kk) * E;
+#pragma unroll
+    for (int q = q0; q < q0 + 4; ++q) {
+      const int e = e0 + 2 * q;
+      uint32_t w;
+      if ((E & 1) == 0)                              // pairs are 4-byte aligned
+        w = e < E ? *reinterpret_cast<const uint32_t*>(row + e) : 0u;
+      else
+        w = (e < E ? row[e] : 0u) | ((e + 1 < E ? static_cast<uint32_t>(row[e + 1]) : 0u) << 16);
+      tile[kk][2 * q] = static_cast<uint16_t>(w & 0xffff);
+      tile[kk][2 * q + 1] = static_cast<uint16_t>(w >> 16);
+    }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int ee = i / 64, kk = i % 64;              // write along k (contiguous in wt)
-    const int64_t k = k0 + kk;
-    const int e = e0 + ee;
-    if (k < d && e < Ep) wt[static_cast<int64_t>(e) * d + k] = tile[kk][ee];
+  {                                                  // write: expert row ee, k pairs
+    const int ee = t >> 2, kq = (t & 3) * 8;
+    if (e0 + ee < Ep) {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(wt + static_cast<int64_t>(e0 + ee) * d + k0 + kq);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        dst[j] = static_cast<uint32_t>(tile[kq + 2 * j][ee]) | (static_cast<uint32_t>(tile[kq + 2 * j + 1][ee]) << 16);
+    }
   }
 }
 
@@ -322,8 +359,16 @@ __global__ __launch_bounds__(256) void route_finish_kernel(const float* __restri
     const int64_t tok = tok0 + t;
     float z = 0.f;
     if (tok < T) {
-      z = partial[tok * E + e];
-      for (int s = 1; s < nsplit; ++s) z += partial[(static_cast<int64_t>(s) * T + tok) * E + e];
+      // issue the loads of up to 16 ranges before the (ordered) additions
+      for (int s0 = 0; s0 < nsplit; s0 += 16) {
+        float v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          v[j] = s0 + j < nsplit ? partial[(static_cast<int64_t>(s0 + j) * T + tok) * E + e] : 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (s0 + j < nsplit) z = (s0 + j == 0) ? v[j] : z + v[j];
+      }
       if (bias) z += bias[e];
       logits[tok * E + e] = z;
     }
@@ -395,7 +440,7 @@ moe_status_t launch_route(const void* x, const void* w_r, const float* bias, int
     if (route_direct(d, dt)) {
       const int Ep = route_padded_experts(E);
       uint16_t* wt = static_cast<uint16_t*>(ws);
-      route_transpose_kernel<<<dim3(static_cast<unsigned>((d + 63) / 64), static_cast<unsigned>((Ep + 63) / 64)), 256,
+      route_transpose_kernel<<<dim3(static_cast<unsigned>(d / 32), static_cast<unsigned>((Ep + 63) / 64)), 256,
                                0, s>>>(static_cast<const uint16_t*>(w_r), d, E, Ep, wt);
       if (moe_status_t st = check_launch("route transpose kernel")) return st;
       set_max_dynamic_smem(reinterpret_cast<const void*>(route_mfma_kernel), smem);
