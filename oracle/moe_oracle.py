@@ -29,9 +29,12 @@ tests/test_oracle_pins.py):
     the probabilities equals the top-k of the logits.  Equal logits: lowest expert
     index first.  Slot j is the j-th best expert.
   * weights are the softmax probabilities of the selected experts renormalised to sum
-    to 1 ([mlqm] §3.3 and §4.2); temperature is 1.
+    to 1 ([mlqm] §3.3 and §4.2); temperature is 1.  Variant: the raw probabilities.
   * capacity keeps, per expert, the earliest tokens (ascending token index); an
     overflowing slot contributes zero and the other weights are not renormalised.
+    Variants: first choices before second choices (slot-major priority), and overflow
+    re-routed to the token's next-best expert with room (router choices first, then the
+    overflow in priority order; a re-routed slot keeps its weight).
   * GeLU is the exact erf form; SwiGLU is down(silu(gate x) * (up x)); experts carry no
     biases; the shared expert is added with weight 1.
 
@@ -40,7 +43,7 @@ Every function here is pinned (see the test module); no function is "parity unpi
 from __future__ import annotations
 
 import math
-from typing import Callable, Dict, Optional, Tuple
+from typing import Callable, Dict, List, Optional, Tuple
 
 import numpy as np
 from scipy.special import erf as _erf
@@ -130,51 +133,97 @@ def capacity_rule(T: int, k: int, E: int, factor: float = 1.0, min_capacity: int
     return max(int(min_capacity), int(math.ceil(factor * T * k / E)))
 
 
-def dispatch(idx: np.ndarray, E: int, capacity: int = 0) -> Dict[str, np.ndarray]:
+def priority_order(T: int, k: int, priority: str = "token") -> List[Tuple[int, int]]:
+    """Order in which slots (t, j) claim capacity.
+
+    "token": ascending token, then slot - the earliest tokens are kept ([rkmt] §2.3 drops
+    the tokens beyond an expert's capacity; arrival order is the plainest reading).
+    "slot": every token's first choice before any second choice, tokens ascending within a
+    slot position (first choices are protected from being displaced by second choices).
+    """
+    if priority == "token":
+        return [(t, j) for t in range(T) for j in range(k)]
+    if priority == "slot":
+        return [(t, j) for j in range(k) for t in range(T)]
+    raise ValueError(priority)
+
+
+def dispatch(idx: np.ndarray, E: int, capacity: int = 0, priority: str = "token",
+             overflow: str = "drop", z: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
     """Group token slots by expert, apply the capacity, build the permutation.
 
-    [rkmt] §2.3: each expert takes at most C tokens; the rest are dropped.  The earliest
-    tokens (ascending token index) are the ones kept.  [200B-5] "四个专家同时算…": every
-    selection is one call of one expert, so sum(counts) = T*k.
+    [rkmt] §2.3: each expert takes at most C tokens; the ones beyond it are dropped, or
+    sent to the next-best expert.  [200B-5] "四个专家同时算…": every selection is one
+    call of one expert, so sum(counts) = T*k.
 
     idx: [T, k] expert per slot.  capacity <= 0 means no limit.
+    Slots claim capacity in priority_order(priority).
+    overflow "drop": a slot beyond its expert's capacity is dropped.
+    overflow "reroute" (needs the logits z [T, E]): first the router's choices claim
+    capacity as with "drop"; then the overflowed slots, in the same priority order, each
+    go to the token's best expert (descending logit, lowest index on ties) that is not
+    among its top-k or its earlier re-routes and still has capacity, else are dropped.
+    A re-routed slot keeps its routing weight.
     Returns
       counts  [E]    number of slots that selected each expert (demand)
-      kept    [E]    min(counts, C)
+      kept    [E]    rows each expert computes
       offsets [E+1]  exclusive prefix sum of kept
-      perm    [R]    row r of the expert-sorted order holds slot t*k+j; rows of one
-                     expert are in ascending token order
+      perm    [R]    row r of the expert-sorted order holds slot t*k+j; the rows of one
+                     expert are its router-chosen slots in priority order, then the
+                     slots re-routed to it in re-route order
       inv     [T,k]  row of slot (t, j), or -1 if the slot was dropped
+      expert  [T,k]  expert that computes slot (t, j), or -1 if dropped
       n_dropped      number of dropped slots
     """
     idx = np.asarray(idx, np.int64)
     T, k = idx.shape
+    order = priority_order(T, k, priority)
+    if overflow not in ("drop", "reroute"):
+        raise ValueError(overflow)
     counts = np.zeros(E, np.int64)
-    arrival = np.zeros((T, k), np.int64)
     for t in range(T):
         for j in range(k):
-            e = int(idx[t, j])
-            arrival[t, j] = counts[e]
-            counts[e] += 1
-    if capacity > 0:
-        keep = arrival < capacity
-        kept = np.minimum(counts, capacity)
-    else:
-        keep = np.ones((T, k), bool)
-        kept = counts.copy()
+            counts[idx[t, j]] += 1
+    expert = np.full((T, k), -1, np.int64)
+    load = np.zeros(E, np.int64)
+    placed = {e: [] for e in range(E)}
+    overflowed = []
+    for t, j in order:                              # the router's choices
+        e = int(idx[t, j])
+        if capacity <= 0 or load[e] < capacity:
+            expert[t, j] = e
+            load[e] += 1
+            placed[e].append((t, j))
+        else:
+            overflowed.append((t, j))
+    if overflow == "reroute" and overflowed:
+        if z is None:
+            raise ValueError("reroute needs the logits")
+        pref = expert_order(z)
+        used = [set(int(e) for e in idx[t]) for t in range(T)]
+        for t, j in overflowed:                     # the next-best experts
+            for e in pref[t]:
+                e = int(e)
+                if e in used[t]:
+                    continue
+                if load[e] < capacity:
+                    expert[t, j] = e
+                    load[e] += 1
+                    placed[e].append((t, j))
+                    used[t].add(e)
+                    break
+    kept = load.copy()
     offsets = np.zeros(E + 1, np.int64)
     offsets[1:] = np.cumsum(kept)
     perm = np.empty(int(offsets[-1]), np.int64)
     inv = np.full((T, k), -1, np.int64)
-    for t in range(T):
-        for j in range(k):
-            if keep[t, j]:
-                e = int(idx[t, j])
-                r = int(offsets[e] + arrival[t, j])
-                perm[r] = t * k + j
-                inv[t, j] = r
-    return dict(counts=counts, kept=kept, offsets=offsets, perm=perm, inv=inv,
-                n_dropped=int((~keep).sum()))
+    for e in range(E):
+        for r, (t, j) in enumerate(placed[e]):
+            row = int(offsets[e]) + r
+            perm[row] = t * k + j
+            inv[t, j] = row
+    return dict(counts=counts, kept=kept, offsets=offsets, perm=perm, inv=inv, expert=expert,
+                n_dropped=int((expert < 0).sum()))
 
 
 # ----------------------------------------------------------------------------------
@@ -261,7 +310,8 @@ def routed_output(x_rows: np.ndarray, idx_rows: np.ndarray, w_rows: np.ndarray,
 def moe_layer(x: np.ndarray, w_r: np.ndarray, k: int, act: str,
               w_gate: np.ndarray, w_up: Optional[np.ndarray], w_down: np.ndarray,
               bias: Optional[np.ndarray] = None, capacity: int = 0,
-              shared: Optional[ExpertWeights] = None, weights: str = "renormalized") -> Dict[str, np.ndarray]:
+              shared: Optional[ExpertWeights] = None, weights: str = "renormalized",
+              priority: str = "token", overflow: str = "drop") -> Dict[str, np.ndarray]:
     """Whole layer: router -> top-k -> weights -> capacity/dispatch -> experts -> combine.
 
     Follows [mlqm] §3.1-§3.3 and §4.2, [rkmt] §2.3 and [200B-5].  Stacked expert weights:
@@ -272,10 +322,10 @@ def moe_layer(x: np.ndarray, w_r: np.ndarray, k: int, act: str,
     z = router_logits(x, w_r, bias)
     idx = select_topk(z, k)
     w = topk_weights(z, idx, weights)
-    disp = dispatch(idx, E, capacity)
+    disp = dispatch(idx, E, capacity, priority, overflow, z)
     keep = disp["inv"] >= 0
     out = routed_output(
-        x, idx, w, keep, act,
+        x, np.where(keep, disp["expert"], idx), w, keep, act,
         lambda e: (w_gate[e], None if w_up is None else w_up[e], w_down[e]),
         shared)
     res = dict(out=out, logits=z, idx=idx, w=w, margin=topk_margin(z, k))

@@ -270,6 +270,75 @@ def check_dispatch():
             np.testing.assert_array_equal(dp["perm"], O.dispatch(idx, E, 0)["perm"])
 
 
+def check_capacity_policies():
+    """Slot-major priority and re-routing of overflow to the next-best expert ([rkmt] §2.3:
+    tokens beyond an expert's capacity are dropped or sent to the next-best expert)."""
+    # worked by hand: 3 tokens choosing both of 2 experts, capacity 1
+    idx = np.array([[0, 1], [1, 0], [1, 0]])
+    tok = O.dispatch(idx, 2, 1, "token")
+    np.testing.assert_array_equal(tok["inv"], [[0, 1], [-1, -1], [-1, -1]])     # token 0 takes both
+    slot = O.dispatch(idx, 2, 1, "slot")
+    np.testing.assert_array_equal(slot["inv"], [[0, -1], [1, -1], [-1, -1]])    # first choices first
+    np.testing.assert_array_equal(slot["perm"], [0, 2])
+    assert tok["n_dropped"] == slot["n_dropped"] == 4
+    # slot-major against library routines: keep the C smallest (slot, token) per expert
+    rng = _rng(11)
+    for (T, E, k, C) in [(30, 5, 2, 4), (40, 4, 3, 7), (17, 6, 2, 0), (25, 3, 2, 100)]:
+        idx = _random_idx(rng, T, E, k, 1.0)
+        dp = O.dispatch(idx, E, C, "slot")
+        tt, jj = np.meshgrid(np.arange(T), np.arange(k), indexing="ij")
+        order = np.lexsort((tt.ravel(), jj.ravel()))          # slot-major positions
+        flat_e = idx.ravel()[order]
+        by_expert = order[np.argsort(flat_e, kind="stable")]   # stable: slot-major within an expert
+        e_sorted = np.sort(flat_e, kind="stable")
+        rank = np.arange(T * k) - np.searchsorted(e_sorted, e_sorted)
+        keep = rank < (C if C > 0 else T * k)
+        np.testing.assert_array_equal(dp["perm"], by_expert[keep])
+        assert dp["n_dropped"] == int((~keep).sum())
+        if C <= 0 or C >= T * k:                               # no drops: only the row order differs
+            np.testing.assert_array_equal(np.sort(dp["perm"]), np.arange(T * k))
+    # re-route worked by hand: 4 tokens all choosing expert 0, capacity 1
+    z = np.array([[3.0, 2, 1], [3, 1, 2], [3, 2, 1], [3, 2, 1]])
+    rr = O.dispatch(np.zeros((4, 1), int), 3, 1, "token", "reroute", z)
+    np.testing.assert_array_equal(rr["expert"], [[0], [2], [1], [-1]])
+    np.testing.assert_array_equal(rr["perm"], [0, 2, 1])
+    np.testing.assert_array_equal(rr["inv"], [[0], [2], [1], [-1]])
+    np.testing.assert_array_equal(rr["kept"], [1, 1, 1])
+    np.testing.assert_array_equal(rr["counts"], [4, 0, 0])
+    assert rr["n_dropped"] == 1
+    # top-k experts and earlier re-routes of the same token are not candidates
+    z = np.array([[4.0, 3, 2, 1], [4, 3, 1, 2]])
+    for pr in ("token", "slot"):
+        rr = O.dispatch(np.array([[0, 1], [0, 1]]), 4, 1, pr, "reroute", z)
+        np.testing.assert_array_equal(rr["expert"], [[0, 1], [3, 2]])
+    # invariants on random cases
+    for (T, E, k, C) in [(40, 6, 2, 5), (60, 8, 3, 9), (33, 5, 2, 3), (50, 4, 1, 10)]:
+        zz = rng.standard_normal((T, E)) + np.linspace(2, 0, E)     # skewed preferences
+        idx = O.select_topk(zz, k)
+        for pr in ("token", "slot"):
+            dr = O.dispatch(idx, E, C, pr, "drop")
+            rr = O.dispatch(idx, E, C, pr, "reroute", zz)
+            np.testing.assert_array_equal(rr["counts"], dr["counts"])
+            assert np.all(rr["kept"] <= C) and rr["n_dropped"] <= dr["n_dropped"]
+            first = dr["inv"] >= 0                                # the router's kept choices stay
+            np.testing.assert_array_equal(rr["expert"][first], idx[first])
+            for t in range(T):
+                ex = [int(e) for e in rr["expert"][t] if e >= 0]
+                assert len(ex) == len(set(ex))                    # distinct experts per token
+                for j in range(k):
+                    e = rr["expert"][t, j]
+                    if not first[t, j] and e >= 0:
+                        assert e not in idx[t]                    # moved off the top-k
+                    if e < 0:                                     # nothing left for it
+                        free = [f for f in range(E) if f not in idx[t] and f not in ex]
+                        assert all(rr["kept"][f] == C for f in free)
+            inv = rr["inv"].ravel()
+            assert np.all(inv[rr["perm"]] == np.arange(len(rr["perm"])))
+        # capacity that never overflows: re-route changes nothing
+        big = O.dispatch(idx, E, T * k, "token", "reroute", zz)
+        np.testing.assert_array_equal(big["perm"], O.dispatch(idx, E, 0)["perm"])
+
+
 def check_activations():
     assert O.gelu(np.array(0.0)) == 0.0 and O.silu(np.array(0.0)) == 0.0
     np.testing.assert_allclose(O.gelu(np.array([1.0, -1.0])),
@@ -395,7 +464,7 @@ def check_routing_stats():
 
 PINS = [check_worked_combine, check_worked_layer, check_printed_gate, check_softmax_weights, check_ln3_weights,
         check_weight_formulations, check_topk_bruteforce, check_topk_margin,
-        check_router_logits, check_capacity_rule, check_dispatch, check_activations,
+        check_router_logits, check_capacity_rule, check_dispatch, check_capacity_policies, check_activations,
         check_expert_ffn, check_layer_special_cases, check_ledgers, check_routing_stats]
 
 
@@ -434,7 +503,7 @@ def _mut_inverted_weights(z, idx, mode="renormalized"):
     return e / e.sum(axis=1, keepdims=True)
 
 
-def _mut_keep_latest(idx, E, capacity=0):
+def _mut_keep_latest(idx, E, capacity=0, priority="token", overflow="drop", z=None):
     res = _orig["dispatch"](idx, E, 0)
     if capacity <= 0:
         return res
@@ -445,6 +514,45 @@ def _mut_keep_latest(idx, E, capacity=0):
 
 def _mut_transposed_down(xr, act, wg, wu, wd):
     return _orig["expert_ffn"](xr, act, wg, wu, np.ascontiguousarray(wd.T).reshape(wd.shape))
+
+
+def _mut_slot_as_token(idx, E, capacity=0, priority="token", overflow="drop", z=None):
+    return _orig["dispatch"](idx, E, capacity, "token", overflow, z)
+
+
+def _mut_reroute_worst(idx, E, capacity=0, priority="token", overflow="drop", z=None):
+    return _orig["dispatch"](idx, E, capacity, priority, overflow, None if z is None else -np.asarray(z))
+
+
+def _mut_reroute_keeps_topk(idx, E, capacity=0, priority="token", overflow="drop", z=None):
+    res = _orig["dispatch"](idx, E, capacity, priority, overflow, z)
+    if overflow != "reroute":
+        return res
+    return _reroute_any(np.asarray(idx), E, capacity, priority, z)
+
+
+def _reroute_any(idx, E, capacity, priority, z):
+    """Planted mistake: overflow may move to the token's own other top-k experts."""
+    T, k = idx.shape
+    expert = np.full((T, k), -1)
+    load = np.zeros(E, int)
+    over = []
+    for t, j in O.priority_order(T, k, priority):
+        e = idx[t, j]
+        if load[e] < capacity:
+            expert[t, j] = e
+            load[e] += 1
+        else:
+            over.append((t, j))
+    pref = O.expert_order(z)
+    for t, j in over:
+        for e in pref[t]:
+            if e not in expert[t] and load[e] < capacity:
+                expert[t, j] = e
+                load[e] += 1
+                break
+    return dict(expert=expert, kept=load, n_dropped=int((expert < 0).sum()), counts=np.bincount(idx.ravel(), minlength=E),
+                perm=np.zeros(0, int), inv=np.full((T, k), -1), offsets=np.zeros(E + 1, int))
 
 
 def _mut_unweighted(y, w, keep=None, shared=None):
@@ -481,7 +589,8 @@ MUTATIONS = [("expert_order", _mut_highest_index_ties), ("topk_weights", _mut_in
              ("combine", _mut_unweighted), ("combine", _mut_no_shared),
              ("router_logits", _mut_bias_dropped), ("gelu", _mut_tanh_gelu),
              ("silu", _mut_sigmoid_only), ("capacity_rule", _mut_capacity_floor_no_k),
-             ("active_params", _mut_ledger_no_k)]
+             ("active_params", _mut_ledger_no_k), ("dispatch", _mut_slot_as_token),
+             ("dispatch", _mut_reroute_worst), ("dispatch", _mut_reroute_keeps_topk)]
 
 
 @pytest.mark.parametrize("name,bad", MUTATIONS, ids=[m[1].__name__ for m in MUTATIONS])
