@@ -65,6 +65,20 @@ typedef enum { MOE_ACT_GELU = 0, MOE_ACT_SWIGLU = 1 } moe_act_t;
  *   MOE_WEIGHTS_SOFTMAX       w_j = p_{s_j}, the softmax probabilities themselves
  *                             ("MoE混合专家架构原理与工程实践…" §3.2: output = p1 e1 + p2 e2) */
 typedef enum { MOE_WEIGHTS_RENORMALIZED = 0, MOE_WEIGHTS_SOFTMAX = 1 } moe_weights_t;
+/* Order in which slots claim expert capacity ([rkmt] §2.3 keeps what fits, drops the rest):
+ *   MOE_PRIORITY_TOKEN  ascending token, then slot: the earliest tokens are kept
+ *   MOE_PRIORITY_SLOT   all first choices, then all second choices, ...; ascending token
+ *                       within one slot position (first choices are never displaced) */
+typedef enum { MOE_PRIORITY_TOKEN = 0, MOE_PRIORITY_SLOT = 1 } moe_priority_t;
+/* What happens to a slot beyond its expert's capacity ([rkmt] §2.3: dropped, or sent to
+ * the next-best expert):
+ *   MOE_OVERFLOW_DROP     the slot contributes zero
+ *   MOE_OVERFLOW_REROUTE  after the router's choices have claimed capacity, the overflowed
+ *                         slots, in priority order, each move to the token's best expert
+ *                         (by logit, lowest index on ties) outside its top-k and its
+ *                         earlier re-routes that still has room, else are dropped; a moved
+ *                         slot keeps its routing weight */
+typedef enum { MOE_OVERFLOW_DROP = 0, MOE_OVERFLOW_REROUTE = 1 } moe_overflow_t;
 
 /* Static description of a status code (host). */
 const char* moe_status_string(moe_status_t s);
@@ -95,29 +109,35 @@ moe_status_t moe_route(const void* x, const void* w_r, const float* bias, moe_dt
                        int32_t* topk_idx, float* topk_w, float* logits, void* ws, size_t ws_bytes,
                        hipStream_t stream);
 
-/* Workspace bytes moe_dispatch needs for T tokens and E experts (host, pure). */
-size_t moe_dispatch_workspace_bytes(int64_t T, int32_t E);
+/* Workspace bytes moe_dispatch needs for T tokens, E experts, k slots, any policy
+ * (host, pure). */
+size_t moe_dispatch_workspace_bytes(int64_t T, int32_t E, int32_t k);
 
 /*
  * moe_dispatch - per-expert counts, capacity, expert-sorted permutation.
- *   [rkmt] §2.3: expert e accepts at most `capacity` slots; the rest are dropped
- *   (zero contribution).  The earliest tokens (ascending token index) are kept.
+ *   [rkmt] §2.3: expert e accepts at most `capacity` slots; the overflow is dropped
+ *   (zero contribution) or re-routed, see moe_priority_t and moe_overflow_t.
  *   topk_idx  [T, k] int32 in  (values in [0, E); other values are undefined behaviour)
+ *   logits    [T, E] fp32 in  (the router logits; read only for MOE_OVERFLOW_REROUTE with
+ *             capacity > 0, may be NULL otherwise)
  *   capacity  <= 0: unlimited
+ *   priority  moe_priority_t; overflow  moe_overflow_t
  *   counts    [E] int32 out: slots that selected e (demand, before capacity)
- *   offsets   [E+1] int32 out: exclusive prefix sum of kept = min(counts, capacity)
- *   perm      [T*k] int32 out: perm[r] = t*k + j for each kept row r < offsets[E];
- *             rows of one expert are in ascending token order; entries >= offsets[E]
- *             are left untouched
+ *   offsets   [E+1] int32 out: exclusive prefix sum of the rows each expert computes
+ *             (min(counts, capacity), plus re-routed arrivals)
+ *   perm      [T*k] int32 out: perm[r] = t*k + j for each row r < offsets[E]; the rows
+ *             of one expert are its router-chosen slots in priority order, then the
+ *             slots re-routed to it in re-route order; entries >= offsets[E] untouched
  *   inv       [T*k] int32 out: row of slot (t, j), or -1 when the slot was dropped
  *   n_dropped [1] int32 out: number of dropped slots
- *   ws        device workspace of at least moe_dispatch_workspace_bytes(T, E) bytes
- * Integer-only and deterministic (bit-identical across runs).
+ *   ws        device workspace of at least moe_dispatch_workspace_bytes(T, E, k) bytes
+ * Integer-only and deterministic (bit-identical across runs).  Re-routing walks the
+ * overflow sequentially in one wave (it is a greedy choice in priority order).
  */
-moe_status_t moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t E, int32_t k,
-                          int64_t capacity, int32_t* counts, int32_t* offsets, int32_t* perm,
-                          int32_t* inv, int32_t* n_dropped, void* ws, size_t ws_bytes,
-                          hipStream_t stream);
+moe_status_t moe_dispatch(const int32_t* topk_idx, const float* logits, int64_t T, int32_t E, int32_t k,
+                          int64_t capacity, moe_priority_t priority, moe_overflow_t overflow,
+                          int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                          int32_t* n_dropped, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes moe_expert_ffn needs (host, pure). */
 size_t moe_expert_ffn_workspace_bytes(int64_t max_rows, int32_t G, int64_t d, int64_t F,
@@ -190,6 +210,8 @@ typedef struct moe_layer_args {
   int32_t out_dt;        /* moe_dtype_t of `out`: MOE_F32 (0, the fp32 accumulator rounded
                             once) or MOE_BF16 (rounded once to bf16) */
   int32_t weights;       /* moe_weights_t (0: renormalised) */
+  int32_t priority;      /* moe_priority_t (0: token order) */
+  int32_t overflow;      /* moe_overflow_t (0: drop) */
   int64_t T, d, F;
   int32_t E, k;
   int64_t capacity;      /* <= 0: unlimited */

@@ -20,6 +20,8 @@ _lib = None
 MOE_F32, MOE_BF16 = 0, 1
 MOE_ACT_GELU, MOE_ACT_SWIGLU = 0, 1
 WEIGHT_MODES = {"renormalized": 0, "softmax": 1}
+PRIORITIES = {"token": 0, "slot": 1}
+OVERFLOWS = {"drop": 0, "reroute": 1}
 STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EUNSUPPORTED", 3: "MOE_EWORKSPACE", 4: "MOE_EHIP"}
 
 # entry points declared in include/moe.h
@@ -38,6 +40,7 @@ class MoEError(RuntimeError):
 
 class LayerArgs(C.Structure):
     _fields_ = [("dt", C.c_int32), ("act", C.c_int32), ("out_dt", C.c_int32), ("weights", C.c_int32),
+                ("priority", C.c_int32), ("overflow", C.c_int32),
                 ("T", C.c_int64), ("d", C.c_int64), ("F", C.c_int64),
                 ("E", C.c_int32), ("k", C.c_int32), ("capacity", C.c_int64),
                 ("x", C.c_void_p), ("w_r", C.c_void_p), ("bias", C.c_void_p),
@@ -80,9 +83,9 @@ def lib():
         L.moe_route.restype = C.c_int
         L.moe_route.argtypes = [vp, vp, vp, C.c_int, i64, i64, i32, i32, C.c_int, vp, vp, vp, vp, sz, vp]
         L.moe_dispatch_workspace_bytes.restype = sz
-        L.moe_dispatch_workspace_bytes.argtypes = [i64, i32]
+        L.moe_dispatch_workspace_bytes.argtypes = [i64, i32, i32]
         L.moe_dispatch.restype = C.c_int
-        L.moe_dispatch.argtypes = [vp, i64, i32, i32, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_dispatch.argtypes = [vp, vp, i64, i32, i32, i64, C.c_int, C.c_int, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_expert_ffn_workspace_bytes.restype = sz
         L.moe_expert_ffn_workspace_bytes.argtypes = [i64, i32, i64, i64, C.c_int, C.c_int]
         L.moe_expert_ffn.restype = C.c_int
@@ -166,18 +169,22 @@ class Dispatch:
     n_dropped: torch.Tensor
 
 
-def dispatch(topk_idx, E, capacity=0) -> Dispatch:
+def dispatch(topk_idx, E, capacity=0, priority="token", overflow="drop", logits=None) -> Dispatch:
+    """priority "token" | "slot"; overflow "drop" | "reroute" (needs the router logits)."""
     _req(topk_idx, "topk_idx", torch.int32)
     T, k = topk_idx.shape
+    if logits is not None:
+        _req(logits, "logits", torch.float32, topk_idx.device)
     dev = topk_idx.device
     counts = torch.empty(E, dtype=torch.int32, device=dev)
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
     perm = torch.full((T * k,), -1, dtype=torch.int32, device=dev)
     inv = torch.empty((T, k), dtype=torch.int32, device=dev)
     nd = torch.empty(1, dtype=torch.int32, device=dev)
-    ws = _ws(lib().moe_dispatch_workspace_bytes(T, E), dev)
-    _check(lib().moe_dispatch(_ptr(topk_idx), T, E, k, int(capacity), _ptr(counts), _ptr(offsets),
-                              _ptr(perm), _ptr(inv), _ptr(nd), _ptr(ws), ws.numel(), _stream(dev)))
+    ws = _ws(lib().moe_dispatch_workspace_bytes(T, E, k), dev)
+    _check(lib().moe_dispatch(_ptr(topk_idx), _ptr(logits), T, E, k, int(capacity), PRIORITIES[priority],
+                              OVERFLOWS[overflow], _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(inv), _ptr(nd),
+                              _ptr(ws), ws.numel(), _stream(dev)))
     return Dispatch(counts, offsets, perm, inv, nd)
 
 
@@ -238,7 +245,8 @@ class Layer:
 
     def __init__(self, w_r, w_gate, w_up, w_down, k, act="swiglu", bias=None, capacity=0,
                  s_gate=None, s_up=None, s_down=None, out_dtype=torch.float32, stats=False,
-                 lambda_balance=0.01, lambda_aux=0.01, gamma_aux=100.0, weights="renormalized"):
+                 lambda_balance=0.01, lambda_aux=0.01, gamma_aux=100.0, weights="renormalized",
+                 priority="token", overflow="drop"):
         self.w_r, self.bias = w_r, bias
         self.w_gate, self.w_up, self.w_down = w_gate, w_up, w_down
         self.s_gate, self.s_up, self.s_down = s_gate, s_up, s_down
@@ -248,6 +256,8 @@ class Layer:
         self.out_dtype = out_dtype
         self.want_stats = bool(stats)
         self.weight_mode = WEIGHT_MODES[weights]
+        self.priority = PRIORITIES[priority]
+        self.overflow = OVERFLOWS[overflow]
         self.stat_coeffs = (lambda_balance, lambda_aux, gamma_aux)
         self.act = MOE_ACT_SWIGLU if act == "swiglu" else MOE_ACT_GELU
         self.E = w_r.shape[1]
@@ -265,6 +275,8 @@ class Layer:
         a.dt, a.act = _dt(x), self.act
         a.out_dt = MOE_BF16 if self.out_dtype == torch.bfloat16 else MOE_F32
         a.weights = self.weight_mode
+        a.priority = self.priority
+        a.overflow = self.overflow
         a.T, a.d, a.F, a.E, a.k, a.capacity = T, self.d, self.F, self.E, self.k, self.capacity
         a.x, a.w_r, a.bias = _ptr(x), _ptr(self.w_r), _ptr(self.bias)
         a.w_gate, a.w_up, a.w_down = _ptr(self.w_gate), _ptr(self.w_up), _ptr(self.w_down)

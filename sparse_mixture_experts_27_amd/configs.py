@@ -25,6 +25,8 @@ class MoEConfig:
     capacity: int = 0       # per-expert capacity, 0 = unlimited
     bias_var: float = 0.0   # variance of the per-expert router offsets, 0 = no offsets
     weights: str = "renormalized"   # "renormalized" | "softmax": routing-weight formulation
+    priority: str = "token"         # "token" | "slot": order in which slots claim capacity
+    overflow: str = "drop"          # "drop" | "reroute": fate of a slot beyond capacity
 
     def scaled(self, **kw) -> "MoEConfig":
         return replace(self, **kw)
@@ -34,7 +36,9 @@ class MoEConfig:
         return (f"{self.name}(T={self.T},d={self.d},E={self.E}{'+1' if self.shared else ''},"
                 f"k={self.k},F={self.F},{self.act},{self.dtype}"
                 f"{',C=%d' % self.capacity if self.capacity else ''}"
-                f"{',w=' + self.weights if self.weights != 'renormalized' else ''})")
+                f"{',w=' + self.weights if self.weights != 'renormalized' else ''}"
+                f"{',' + self.priority + '-major' if self.priority != 'token' else ''}"
+                f"{',' + self.overflow if self.overflow != 'drop' else ''})")
 
 
 CONFIGS = {

@@ -132,14 +132,15 @@ moe_status_t moe_route(const void* x, const void* w_r, const float* bias, moe_dt
   return launch_route(x, w_r, bias, dt, T, d, E, k, weights, topk_idx, topk_w, logits, ws, stream);
 }
 
-size_t moe_dispatch_workspace_bytes(int64_t T, int32_t E) {
-  if (T < 0 || E < 1) return 0;
-  return dispatch_ws_bytes(T, E);
+size_t moe_dispatch_workspace_bytes(int64_t T, int32_t E, int32_t k) {
+  if (T < 0 || E < 1 || k < 1) return 0;
+  return dispatch_ws_bytes(T, E, k);
 }
 
-moe_status_t moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t E, int32_t k, int64_t capacity,
-                          int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* n_dropped,
-                          void* ws, size_t ws_bytes, hipStream_t stream) {
+moe_status_t moe_dispatch(const int32_t* topk_idx, const float* logits, int64_t T, int32_t E, int32_t k,
+                          int64_t capacity, moe_priority_t priority, moe_overflow_t overflow, int32_t* counts,
+                          int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* n_dropped, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
   g_last_error[0] = 0;
   if (T < 0 || T > (int64_t{1} << 31) - 1) return fail(MOE_EINVAL, "T out of range");
   if (E < 1 || E > kMaxExperts) return fail(MOE_EINVAL, "E=%d must be in [1, %d]", E, kMaxExperts);
@@ -147,10 +148,19 @@ moe_status_t moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t E, int32_t
   if (T * k > (int64_t{1} << 31) - 1) return fail(MOE_EINVAL, "T*k exceeds 2^31-1");
   if (!counts || !offsets || !n_dropped || !ws || (T > 0 && (!topk_idx || !perm || !inv)))
     return fail(MOE_EINVAL, "moe_dispatch: null required pointer");
-  const size_t need = dispatch_ws_bytes(T, E);
-  if (ws_bytes < need) return fail(MOE_EWORKSPACE, "dispatch needs %zu workspace bytes, got %zu", need, ws_bytes);
+  if (priority != MOE_PRIORITY_TOKEN && priority != MOE_PRIORITY_SLOT)
+    return fail(MOE_EINVAL, "priority %d invalid", priority);
+  if (overflow != MOE_OVERFLOW_DROP && overflow != MOE_OVERFLOW_REROUTE)
+    return fail(MOE_EINVAL, "overflow %d invalid", overflow);
   if (capacity > (int64_t{1} << 31) - 1) capacity = 0;   // larger than any count: unlimited
-  return launch_dispatch(topk_idx, T, E, k, capacity, counts, offsets, perm, inv, n_dropped, ws, stream);
+  if (overflow == MOE_OVERFLOW_REROUTE && capacity > 0 && T > 0 && !logits)
+    return fail(MOE_EINVAL, "re-routing needs the router logits");
+  if (overflow == MOE_OVERFLOW_REROUTE && T * k > (int64_t{1} << 29))
+    return fail(MOE_EUNSUPPORTED, "re-routing supports at most 2^29 slots");
+  const size_t need = dispatch_ws_bytes(T, E, k);
+  if (ws_bytes < need) return fail(MOE_EWORKSPACE, "dispatch needs %zu workspace bytes, got %zu", need, ws_bytes);
+  return launch_dispatch(topk_idx, logits, T, E, k, capacity, priority, overflow, counts, offsets, perm, inv,
+                         n_dropped, ws, stream);
 }
 
 size_t moe_expert_ffn_workspace_bytes(int64_t max_rows, int32_t G, int64_t d, int64_t F, moe_act_t act,
@@ -218,7 +228,7 @@ static size_t layer_layout(const moe_layer_args_t* a, bool carve, WsCarver& c, i
   int32_t* nd = c.take<int32_t>(1);
   void* rw = c.take<char>(route_ws_bytes(T, a->d, a->E, a->dt));
   void* sw = c.take<char>(a->stats ? stats_ws_bytes(T) : 0);
-  void* dw = c.take<char>(dispatch_ws_bytes(T, a->E));
+  void* dw = c.take<char>(dispatch_ws_bytes(T, a->E, a->k));
   float* yy = c.take<float>(static_cast<size_t>(plan->splits) * max_rows * a->d);
   void* fw = c.take<char>(plan->ws_bytes);
   if (carve) {
@@ -257,6 +267,12 @@ moe_status_t moe_layer_forward(const moe_layer_args_t* a, hipStream_t stream) {
   if (!valid_dt(a->out_dt)) return fail(MOE_EINVAL, "out dtype %d invalid", a->out_dt);
   if (a->weights != MOE_WEIGHTS_RENORMALIZED && a->weights != MOE_WEIGHTS_SOFTMAX)
     return fail(MOE_EINVAL, "weights mode %d invalid", a->weights);
+  if (a->priority != MOE_PRIORITY_TOKEN && a->priority != MOE_PRIORITY_SLOT)
+    return fail(MOE_EINVAL, "priority %d invalid", a->priority);
+  if (a->overflow != MOE_OVERFLOW_DROP && a->overflow != MOE_OVERFLOW_REROUTE)
+    return fail(MOE_EINVAL, "overflow %d invalid", a->overflow);
+  if (a->overflow == MOE_OVERFLOW_REROUTE && a->T * a->k > (int64_t{1} << 29))
+    return fail(MOE_EUNSUPPORTED, "re-routing supports at most 2^29 slots");
   if (a->F < 1) return fail(MOE_EINVAL, "F must be >= 1");
   if (a->dt == MOE_BF16 && (a->d % 64 != 0 || a->F % 64 != 0))
     return fail(MOE_EUNSUPPORTED, "bf16 layer needs d and F multiples of 64");
@@ -300,7 +316,8 @@ moe_status_t moe_layer_forward(const moe_layer_args_t* a, hipStream_t stream) {
                                      rws, stream))
     return st;
   mark(1);
-  if (moe_status_t st = launch_dispatch(idx, T, a->E, a->k, capacity, counts, offsets, perm, inv, ndrop, dws, stream))
+  if (moe_status_t st = launch_dispatch(idx, logits, T, a->E, a->k, capacity, a->priority, a->overflow, counts,
+                                        offsets, perm, inv, ndrop, dws, stream))
     return st;
   if (a->stats) {
     if (moe_status_t st = launch_stats(logits, counts, ndrop, T, a->E, a->k, a->lambda_balance, a->lambda_aux,

@@ -49,10 +49,10 @@ moe_status_t launch_route(const void* x, const void* w_r, const float* bias, int
                           int64_t T, int64_t d, int E, int k, int mode, int32_t* topk_idx,
                           float* topk_w, float* logits, void* ws, hipStream_t s);
 
-size_t dispatch_ws_bytes(int64_t T, int E);
-moe_status_t launch_dispatch(const int32_t* topk_idx, int64_t T, int E, int k, int64_t capacity,
-                             int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
-                             int32_t* n_dropped, void* ws, hipStream_t s);
+size_t dispatch_ws_bytes(int64_t T, int E, int k);
+moe_status_t launch_dispatch(const int32_t* topk_idx, const float* logits, int64_t T, int E, int k,
+                             int64_t capacity, int priority, int overflow, int32_t* counts, int32_t* offsets,
+                             int32_t* perm, int32_t* inv, int32_t* n_dropped, void* ws, hipStream_t s);
 
 // One FFN problem: G routed groups (rows from `offsets`, gathered through `perm`)
 // plus an optional shared group of `shared_rows` identity rows placed at row

@@ -1,34 +1,54 @@
 // Dispatch: per-expert counts, capacity, expert-sorted permutation.
 // [rkmt] "大模型MoE架构揭秘：为什么总参数≠激活参数" §2.3: each expert takes at most C
-// slots, the overflow is dropped; [200B-5] "四个专家同时算，选两个会更快吗？": every
-// selection is one call of one expert.  The kept slots of one expert are the earliest
-// tokens, laid out in ascending token order (a stable counting sort by expert).
+// slots; the overflow is dropped or sent to the next-best expert; [200B-5]
+// "四个专家同时算，选两个会更快吗？": every selection is one call of one expert.
+//
+// Slots claim capacity in a priority order: token-major (ascending token, then slot) or
+// slot-major (all first choices, then all second choices, ...; ascending token within a
+// slot position).  The passes walk "virtual tokens" in that order: token-major, virtual
+// token u is token u with its k slots; slot-major, u = j*T + t is the single slot (t, j).
+// The kept slots of one expert are laid out in priority order (a stable counting sort).
 //
 // Three integer-only passes, bit-deterministic:
-//   1. count:   per block of 256 tokens, LDS histogram -> block_counts[b][e]
+//   1. count:   per block of 256 virtual tokens, LDS histogram -> block_counts[b][e]
 //   2. scan:    per expert, exclusive scan over blocks -> block_base[b][e]; counts,
 //               kept = min(counts, C), offsets = exclusive scan of kept, n_dropped
 //   3. scatter: rank of each slot inside its expert = block_base + earlier waves of
 //               the block + earlier lanes of the wave; kept slots go to
 //               perm[offsets[e] + rank], inv gets the row or -1
-// A batch of at most 256 tokens runs all three in one workgroup.
+// A batch of at most 256 virtual tokens runs all three in one workgroup.
+// Re-routing adds two passes: one wave walks the overflowed slots in priority order and
+// gives each the best expert (by logit, lowest index on ties) outside the token's top-k
+// and earlier re-routes that still has room; then every slot's row is rebuilt, with
+// the router-chosen rows of an expert first and its re-routed arrivals after them.
 #include "moe_common.h"
 
 namespace moe {
 namespace {
 
-constexpr int DP_TOK = 256;   // tokens per block (4 waves x 64 lanes, one token per lane)
+constexpr int DP_TOK = 256;   // virtual tokens per block (4 waves x 64 lanes, one per lane)
 
-__global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __restrict__ idx,
-                                                             int64_t T, int E, int k,
+// Slot addressing in priority order (see above).
+struct SlotMap {
+  int64_t T;
+  int k;
+  bool slot_major;
+  __device__ int64_t ntok() const { return slot_major ? T * k : T; }
+  __device__ int kv() const { return slot_major ? 1 : k; }
+  __device__ int64_t slot(int64_t u, int jv) const {
+    return slot_major ? (u % T) * k + u / T : u * k + jv;
+  }
+};
+
+__global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __restrict__ idx, SlotMap m, int E,
                                                              int32_t* __restrict__ block_counts) {
   __shared__ int32_t cnt[kMaxExperts];
   for (int e = threadIdx.x; e < E; e += 256) cnt[e] = 0;
   __syncthreads();
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * DP_TOK + threadIdx.x;
-  if (t < T)
-    for (int j = 0; j < k; ++j) {
-      const int32_t e = idx[t * k + j];
+  const int64_t u = static_cast<int64_t>(blockIdx.x) * DP_TOK + threadIdx.x;
+  if (u < m.ntok())
+    for (int j = 0; j < m.kv(); ++j) {
+      const int32_t e = idx[m.slot(u, j)];
       if (static_cast<uint32_t>(e) < static_cast<uint32_t>(E)) atomicAdd(&cnt[e], 1);
     }
   __syncthreads();
@@ -82,30 +102,31 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
 // hold the per-wave demand of this block; block_base(e) is the number of earlier tokens
 // (in earlier blocks) that chose e, offsets[e] the first row of e.
 template <typename BaseFn>
-__device__ void scatter_block(const int32_t* __restrict__ idx, int64_t T, int E, int k, int64_t capacity,
+__device__ void scatter_block(const int32_t* __restrict__ idx, SlotMap m, int E, int64_t capacity,
                               BaseFn block_base, const int32_t* offsets, int32_t (*wcnt)[kMaxExperts],
                               int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * DP_TOK + threadIdx.x;
-  const bool valid = t < T;
-  for (int j = 0; j < k; ++j) {
-    int32_t e = valid ? idx[t * k + j] : -1;
+  const int64_t u = static_cast<int64_t>(blockIdx.x) * DP_TOK + threadIdx.x;
+  const bool valid = u < m.ntok();
+  const int kv = m.kv();
+  for (int j = 0; j < kv; ++j) {
+    int32_t e = valid ? idx[m.slot(u, j)] : -1;
     if (static_cast<uint32_t>(e) >= static_cast<uint32_t>(E)) e = -1;   // ignored slot
-    // lanes below me (earlier tokens of this wave) that selected e in any slot; a
-    // token never selects one expert twice
+    // lanes below me (earlier virtual tokens of this wave) that selected e in any of
+    // their slots; a token never selects one expert twice
     int32_t rank = 0;
-    for (int j2 = 0; j2 < k; ++j2) {
-      const int32_t v = valid ? idx[t * k + j2] : -2;
+    for (int j2 = 0; j2 < kv; ++j2) {
+      const int32_t v = valid ? idx[m.slot(u, j2)] : -2;
       for (int src = 0; src < 64; ++src) {
         const int32_t es = __shfl(v, src);
         rank += (src < lane && es == e) ? 1 : 0;
       }
     }
-    if (valid && e < 0) inv[t * k + j] = -1;
+    if (valid && e < 0) inv[m.slot(u, j)] = -1;
     if (e >= 0) {
       int32_t r = block_base(e) + rank;
       for (int w = 0; w < wave; ++w) r += wcnt[w][e];
-      const int64_t slot = t * k + j;
+      const int64_t slot = m.slot(u, j);
       if (capacity > 0 && r >= capacity) {
         inv[slot] = -1;
       } else {
@@ -118,40 +139,39 @@ __device__ void scatter_block(const int32_t* __restrict__ idx, int64_t T, int E,
 }
 
 // Per-wave demand of this block into wcnt (zeroed here).
-__device__ void count_block(const int32_t* __restrict__ idx, int64_t T, int E, int k,
-                            int32_t (*wcnt)[kMaxExperts]) {
+__device__ void count_block(const int32_t* __restrict__ idx, SlotMap m, int E, int32_t (*wcnt)[kMaxExperts]) {
   const int wave = threadIdx.x >> 6;
   for (int i = threadIdx.x; i < 4 * E; i += 256) wcnt[i / E][i % E] = 0;
   __syncthreads();
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * DP_TOK + threadIdx.x;
-  if (t < T)
-    for (int j = 0; j < k; ++j) {
-      const int32_t e = idx[t * k + j];
+  const int64_t u = static_cast<int64_t>(blockIdx.x) * DP_TOK + threadIdx.x;
+  if (u < m.ntok())
+    for (int j = 0; j < m.kv(); ++j) {
+      const int32_t e = idx[m.slot(u, j)];
       if (static_cast<uint32_t>(e) < static_cast<uint32_t>(E)) atomicAdd(&wcnt[wave][e], 1);
     }
   __syncthreads();
 }
 
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
-    const int32_t* __restrict__ idx, int64_t T, int E, int k, int64_t capacity,
+    const int32_t* __restrict__ idx, SlotMap m, int E, int64_t capacity,
     const int32_t* __restrict__ block_base, const int32_t* __restrict__ offsets,
     int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
   __shared__ int32_t wcnt[4][kMaxExperts];
-  count_block(idx, T, E, k, wcnt);
+  count_block(idx, m, E, wcnt);
   const int32_t* bb = block_base + static_cast<int64_t>(blockIdx.x) * E;
-  scatter_block(idx, T, E, k, capacity, [&](int e) { return bb[e]; }, offsets, wcnt, perm, inv);
+  scatter_block(idx, m, E, capacity, [&](int e) { return bb[e]; }, offsets, wcnt, perm, inv);
 }
 
 // All of dispatch in one workgroup when the batch fits one block (T <= 256): demand,
 // kept counts, offsets and drops are computed in LDS, then the slots are placed.
 __global__ __launch_bounds__(256) void dispatch_small_kernel(
-    const int32_t* __restrict__ idx, int64_t T, int E, int k, int64_t capacity,
+    const int32_t* __restrict__ idx, SlotMap m, int E, int64_t capacity,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
     int32_t* __restrict__ inv, int32_t* __restrict__ n_dropped) {
   __shared__ int32_t wcnt[4][kMaxExperts];
   __shared__ int32_t off[kMaxExperts + 1];
   __shared__ int32_t wsum[4], wdrop[4];
-  count_block(idx, T, E, k, wcnt);
+  count_block(idx, m, E, wcnt);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // thread i owns experts 4i .. 4i+3 (E <= 1024)
   int32_t kept_loc[4];
@@ -199,37 +219,283 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(
     *n_dropped = wdrop[0] + wdrop[1] + wdrop[2] + wdrop[3];
   }
   __syncthreads();
-  scatter_block(idx, T, E, k, capacity, [](int) { return 0; }, off, wcnt, perm, inv);
+  scatter_block(idx, m, E, capacity, [](int) { return 0; }, off, wcnt, perm, inv);
+}
+
+// ---- re-routing of the overflow -------------------------------------------------
+// Wave-wide maximum of a 64-bit key (hi, lo) with DPP lane moves (no LDS round trips):
+// maxima inside 16-lane rows (quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E, row_ror:4 =
+// 0x124, row_ror:8 = 0x128), then across rows (row_bcast:15 = 0x142 into rows 1 and 3,
+// row_bcast:31 = 0x143 into rows 2 and 3); lane 63 ends with the maximum, which is
+// returned to every lane.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void key_max_dpp(uint32_t& hi, uint32_t& lo) {
+  const uint32_t ohi = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(static_cast<int>(hi), static_cast<int>(hi), CTRL, ROWS, 0xF, false));
+  const uint32_t olo = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(static_cast<int>(lo), static_cast<int>(lo), CTRL, ROWS, 0xF, false));
+  if (ohi > hi || (ohi == hi && olo > lo)) { hi = ohi; lo = olo; }
+}
+__device__ __forceinline__ void wave_key_max(uint32_t& hi, uint32_t& lo) {
+  key_max_dpp<0xB1, 0xF>(hi, lo);
+  key_max_dpp<0x4E, 0xF>(hi, lo);
+  key_max_dpp<0x124, 0xF>(hi, lo);
+  key_max_dpp<0x128, 0xF>(hi, lo);
+  key_max_dpp<0x142, 0xA>(hi, lo);
+  key_max_dpp<0x143, 0xC>(hi, lo);
+  hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(hi), 63));
+  lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lo), 63));
+}
+
+__device__ __forceinline__ uint32_t dp_ordered_key(float z) {
+  uint32_t b = __float_as_uint(z);
+  if (b == 0x80000000u) b = 0u;                       // -0 ties with +0
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// One wave.  Walks the slots in priority order; a slot with a valid expert and no row
+// (inv < 0 after the capacity pass) takes the best expert outside its token's top-k and
+// the token's earlier re-routes that still has room.  Writes target[slot] (-1: still
+// dropped), arrival[slot] (rank among the expert's re-routed arrivals), the new offsets
+// (kept + arrivals; the capacity pass's offsets are saved to off1 first) and n_dropped.
+// The walk goes in chunks of 64 priority positions; the logits and top-k rows of a
+// chunk's overflowed slots are first staged into LDS together (one memory round trip
+// per chunk, not per slot).  The experts a token already uses live in an LDS flag array:
+// in token-major order a token's slots are consecutive, so the flags carry over between
+// them; in slot-major order the targets of the token's earlier slot positions come from
+// an LDS copy of `target` (when T*k fits) or are read back from memory past L1 after the
+// stores that wrote them have completed.  One wave's LDS accesses execute in issue
+// order, so flag and counter updates need only compiler ordering (signal fences).
+struct RerouteLds {
+  int chunk;         // priority positions per chunk (64, 32, 16 or 8)
+  int stage_e;       // E (row length of the staged logits)
+  int stage_k;       // k
+  bool tcache;       // LDS copy of target[T*k] follows the staging area
+};
+
+// Dynamic LDS of the re-route pass: the staging rows of one chunk (at most 96 KB: the
+// chunk shrinks for wide rows) and, in slot-major order, the target copy when it fits
+// in the rest of 140 KB (the kernel's static arrays take another 16.5 KB of the 160 KB).
+size_t reroute_lds_bytes(int64_t T, int E, int k, bool slot_major, RerouteLds& cfg) {
+  const size_t row = static_cast<size_t>(E + k) * sizeof(int32_t);
+  int chunk = 64;
+  while (chunk > 8 && chunk * row > 96 * 1024) chunk /= 2;
+  const size_t stage = chunk * row;
+  const size_t tc = static_cast<size_t>(T) * k * sizeof(int32_t);
+  cfg.chunk = chunk;
+  cfg.stage_e = E;
+  cfg.stage_k = k;
+  cfg.tcache = slot_major && stage + tc <= 140 * 1024;
+  return stage + (cfg.tcache ? tc : 0);
+}
+
+__global__ __launch_bounds__(64) void dispatch_reroute_kernel(
+    const int32_t* __restrict__ idx, const float* __restrict__ logits, SlotMap m, int E, int64_t capacity,
+    RerouteLds lc, const int32_t* __restrict__ inv, int32_t* __restrict__ offsets, int32_t* __restrict__ off1,
+    int32_t* __restrict__ target, int32_t* __restrict__ arrival, int32_t* __restrict__ n_dropped) {
+  __shared__ int32_t room[kMaxExperts];
+  __shared__ int32_t arr[kMaxExperts];
+  __shared__ int32_t used[kMaxExperts];
+  __shared__ int32_t kept1[kMaxExperts];
+  __shared__ int64_t ctok[64];                       // token of each staged slot (-1: none)
+  extern __shared__ __attribute__((aligned(16))) int32_t dyn[];
+  float* zst = reinterpret_cast<float*>(dyn);        // [chunk][E] staged logits rows
+  int32_t* kst = dyn + lc.chunk * lc.stage_e;        // [chunk][k] staged top-k rows
+  int32_t* tcache = kst + lc.chunk * lc.stage_k;     // [T*k] when lc.tcache
+  const int CH = lc.chunk;
+  const int lane = threadIdx.x;
+  const int k = m.k;
+  const int64_t nslots = m.T * k;
+  for (int e = lane; e <= E; e += 64) off1[e] = offsets[e];
+  for (int e = lane; e < E; e += 64) {
+    kept1[e] = offsets[e + 1] - offsets[e];
+    room[e] = static_cast<int32_t>(capacity) - kept1[e];
+    arr[e] = 0;
+  }
+  for (int64_t s = lane; s < nslots; s += 64) {
+    target[s] = -1;
+    if (lc.tcache) tcache[s] = -1;
+  }
+  const __amdgpu_buffer_rsrc_t trs =
+      __builtin_amdgcn_make_buffer_rsrc(target, static_cast<short>(0), 0x7FFFFFFF, 0x00020000);
+  __builtin_amdgcn_s_waitcnt(0);                      // target initialised before any read-back
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  const int32_t dropped1 = *n_dropped;
+  int32_t moved = 0;
+  int64_t cur_t = -1;
+  // priority position p -> slot: token-major p itself, slot-major (p % T)*k + p / T;
+  // lane i of a chunk holds position p0 + i (i < CH)
+  for (int64_t p0 = 0; p0 < nslots; p0 += CH) {
+    const int64_t p = p0 + lane;
+    int32_t slot = -1, tok = -1, jj = 0;              // T*k < 2^29 for re-routing (host check)
+    bool over = false;
+    if (lane < CH && p < nslots) {
+      slot = static_cast<int32_t>(m.slot_major ? (p % m.T) * k + p / m.T : p);
+      tok = slot / k;
+      jj = slot - tok * k;
+      const int32_t e = idx[slot];
+      over = static_cast<uint32_t>(e) < static_cast<uint32_t>(E) && inv[slot] < 0;
+    }
+    uint64_t mask = __ballot(over);
+    if (!mask) continue;
+    // stage the logits and top-k rows of this chunk's overflowed slots
+    ctok[lane] = over ? tok : -1;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    for (int f = lane; f < CH * E; f += 64) {
+      const int64_t t = ctok[f / E];
+      if (t >= 0) zst[f] = logits[t * E + f % E];
+    }
+    for (int f = lane; f < CH * k; f += 64) {
+      const int64_t t = ctok[f / k];
+      if (t >= 0) kst[f] = idx[t * k + f % k];
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    while (mask) {                                    // lowest lane first = priority order
+      const int src = __builtin_ctzll(mask);
+      mask &= mask - 1;
+      const int32_t sl = __builtin_amdgcn_readlane(slot, src);
+      const int64_t t = __builtin_amdgcn_readlane(tok, src);
+      const int j = __builtin_amdgcn_readlane(jj, src);
+      if (m.slot_major || t != cur_t) {               // flags of a new token: its top-k ...
+        cur_t = t;
+        for (int e = lane; e < E; e += 64) used[e] = 0;
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        for (int q = lane; q < k; q += 64) {
+          const int32_t eq = kst[src * k + q];
+          if (static_cast<uint32_t>(eq) < static_cast<uint32_t>(E)) used[eq] = 1;
+          // ... and, in slot-major order, the targets of its earlier slot positions
+          if (m.slot_major && q < j) {
+            const int32_t tg = lc.tcache ? tcache[t * k + q]
+                                         : __builtin_amdgcn_raw_buffer_load_b32(
+                                               trs, static_cast<int>((t * k + q) * 4), 0, 1 /* glc: past L1 */);
+            if (tg >= 0) used[tg] = 1;
+          }
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      }
+      uint32_t bhi = 0, blo = 0;
+      for (int e = lane; e < E; e += 64) {
+        if (room[e] <= 0 || used[e]) continue;
+        const uint32_t hi = dp_ordered_key(zst[src * E + e]);
+        const uint32_t lo = 0xffffffffu - static_cast<uint32_t>(e);
+        if (hi > bhi || (hi == bhi && lo > blo)) { bhi = hi; blo = lo; }
+      }
+      wave_key_max(bhi, blo);
+      if (bhi != 0) {                                 // an expert with room was found
+        const int32_t e = static_cast<int32_t>(0xffffffffu - blo);
+        const int32_t a = arr[e];
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (lane == 0) {
+          room[e] = room[e] - 1;
+          arr[e] = a + 1;
+          used[e] = 1;
+          if (lc.tcache) tcache[sl] = e;
+          target[sl] = e;
+          arrival[sl] = a;
+        }
+        ++moved;
+        if (m.slot_major && !lc.tcache) __builtin_amdgcn_s_waitcnt(0);   // before any read-back
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      }
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);          // staging area reused by the next chunk
+  }
+  // new offsets: kept + arrivals, exclusive scan over experts (lane owns a range)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  const int per = (E + 63) / 64;
+  int32_t local = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = lane * per + i;
+    if (e < E) local += kept1[e] + arr[e];
+  }
+  int32_t incl = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t x = __shfl_up(incl, o);
+    if (lane >= o) incl += x;
+  }
+  int32_t run = incl - local;
+  for (int i = 0; i < per; ++i) {
+    const int e = lane * per + i;
+    if (e < E) {
+      offsets[e] = run;
+      run += kept1[e] + arr[e];
+    }
+  }
+  if (lane == 63) offsets[E] = incl;
+  if (lane == 0) *n_dropped = dropped1 - moved;
+}
+
+// Rebuild rows after re-routing: a router-chosen kept slot keeps its rank inside its
+// expert; a re-routed slot goes after its new expert's router-chosen rows.
+__global__ __launch_bounds__(256) void dispatch_rebuild_kernel(
+    const int32_t* __restrict__ idx, int64_t nslots, int E, const int32_t* __restrict__ off1,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ target,
+    const int32_t* __restrict__ arrival, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  const int64_t s = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (s >= nslots) return;
+  const int32_t r1 = inv[s];
+  int32_t row = -1;
+  if (r1 >= 0) {
+    const int32_t e = idx[s];
+    row = offsets[e] + (r1 - off1[e]);
+  } else {
+    const int32_t e = target[s];
+    if (e >= 0) row = offsets[e] + (off1[e + 1] - off1[e]) + arrival[s];
+  }
+  inv[s] = row;
+  if (row >= 0) perm[row] = static_cast<int32_t>(s);
 }
 
 }  // namespace
 
-size_t dispatch_ws_bytes(int64_t T, int E) {
-  const int64_t nb = (T + DP_TOK - 1) / DP_TOK;
-  return 2 * align_up(static_cast<size_t>(nb) * E * sizeof(int32_t), 256);
+// Workspace for every policy: block tables sized for T*k virtual tokens, the saved
+// offsets and the per-slot re-route target and arrival rank.
+size_t dispatch_ws_bytes(int64_t T, int E, int k) {
+  const int64_t nb = (T * k + DP_TOK - 1) / DP_TOK;
+  return 2 * align_up(static_cast<size_t>(nb) * E * sizeof(int32_t), 256) +
+         align_up(static_cast<size_t>(E + 1) * sizeof(int32_t), 256) +
+         2 * align_up(static_cast<size_t>(T) * k * sizeof(int32_t), 256);
 }
 
-moe_status_t launch_dispatch(const int32_t* topk_idx, int64_t T, int E, int k, int64_t capacity,
-                             int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
-                             int32_t* n_dropped, void* ws, hipStream_t s) {
-  const int64_t nb = (T + DP_TOK - 1) / DP_TOK;
+moe_status_t launch_dispatch(const int32_t* topk_idx, const float* logits, int64_t T, int E, int k,
+                             int64_t capacity, int priority, int overflow, int32_t* counts, int32_t* offsets,
+                             int32_t* perm, int32_t* inv, int32_t* n_dropped, void* ws, hipStream_t s) {
+  const SlotMap m{T, k, priority == MOE_PRIORITY_SLOT};
+  const int64_t ntok = m.slot_major ? T * k : T;
+  const int64_t nb = (ntok + DP_TOK - 1) / DP_TOK;
+  const int64_t nb_max = (T * k + DP_TOK - 1) / DP_TOK;
   WsCarver c(ws);
-  int32_t* block_counts = c.take<int32_t>(static_cast<size_t>(nb) * E);
-  int32_t* block_base = c.take<int32_t>(static_cast<size_t>(nb) * E);
+  int32_t* block_counts = c.take<int32_t>(static_cast<size_t>(nb_max) * E);
+  int32_t* block_base = c.take<int32_t>(static_cast<size_t>(nb_max) * E);
+  int32_t* off1 = c.take<int32_t>(static_cast<size_t>(E) + 1);
+  int32_t* target = c.take<int32_t>(static_cast<size_t>(T) * k);
+  int32_t* arrival = c.take<int32_t>(static_cast<size_t>(T) * k);
   if (nb <= 1) {
-    const int64_t Tg = nb == 0 ? 0 : T;
-    dispatch_small_kernel<<<1, 256, 0, s>>>(topk_idx, Tg, E, k, capacity, counts, offsets, perm, inv, n_dropped);
-    return check_launch("dispatch kernel");
+    const SlotMap mg{nb == 0 ? 0 : T, k, m.slot_major};
+    dispatch_small_kernel<<<1, 256, 0, s>>>(topk_idx, mg, E, capacity, counts, offsets, perm, inv, n_dropped);
+    if (moe_status_t st = check_launch("dispatch kernel")) return st;
+  } else {
+    dispatch_count_kernel<<<static_cast<unsigned>(nb), 256, 0, s>>>(topk_idx, m, E, block_counts);
+    if (moe_status_t st = check_launch("dispatch count kernel")) return st;
+    dispatch_scan_kernel<<<1, 1024, 0, s>>>(block_counts, static_cast<int>(nb), E, capacity, block_base,
+                                            counts, offsets, n_dropped);
+    if (moe_status_t st = check_launch("dispatch scan kernel")) return st;
+    dispatch_scatter_kernel<<<static_cast<unsigned>(nb), 256, 0, s>>>(topk_idx, m, E, capacity,
+                                                                      block_base, offsets, perm, inv);
+    if (moe_status_t st = check_launch("dispatch scatter kernel")) return st;
   }
-  dispatch_count_kernel<<<static_cast<unsigned>(nb), 256, 0, s>>>(topk_idx, T, E, k, block_counts);
-  if (moe_status_t st = check_launch("dispatch count kernel")) return st;
-  dispatch_scan_kernel<<<1, 1024, 0, s>>>(block_counts, static_cast<int>(nb), E, capacity, block_base,
-                                          counts, offsets, n_dropped);
-  if (moe_status_t st = check_launch("dispatch scan kernel")) return st;
-  dispatch_scatter_kernel<<<static_cast<unsigned>(nb), 256, 0, s>>>(topk_idx, T, E, k, capacity,
-                                                                    block_base, offsets, perm, inv);
-  if (moe_status_t st = check_launch("dispatch scatter kernel")) return st;
-  return MOE_OK;
+  if (overflow != MOE_OVERFLOW_REROUTE || capacity <= 0 || T == 0) return MOE_OK;
+  RerouteLds lc{};
+  const size_t lds = reroute_lds_bytes(T, E, k, m.slot_major, lc);
+  set_max_dynamic_smem(reinterpret_cast<const void*>(dispatch_reroute_kernel), lds);
+  dispatch_reroute_kernel<<<1, 64, lds, s>>>(topk_idx, logits, m, E, capacity, lc, inv, offsets, off1, target,
+                                             arrival, n_dropped);
+  if (moe_status_t st = check_launch("dispatch re-route kernel")) return st;
+  const int64_t nslots = T * k;
+  dispatch_rebuild_kernel<<<static_cast<unsigned>((nslots + 255) / 256), 256, 0, s>>>(
+      topk_idx, nslots, E, off1, offsets, target, arrival, perm, inv);
+  return check_launch("dispatch rebuild kernel");
 }
 
 }  // namespace moe

@@ -40,7 +40,8 @@ def say(msg: str):
 def layer_for(cfg, inp, out_dtype=torch.float32):
     return B.Layer(inp["w_r"], inp["w_gate"], inp["w_up"], inp["w_down"], cfg.k, act=cfg.act,
                    bias=inp["bias"], capacity=cfg.capacity, s_gate=inp["s_gate"], s_up=inp["s_up"],
-                   s_down=inp["s_down"], out_dtype=out_dtype, weights=cfg.weights)
+                   s_down=inp["s_down"], out_dtype=out_dtype, weights=cfg.weights, priority=cfg.priority,
+                   overflow=cfg.overflow)
 
 
 def half_ulp_bf16(v: np.ndarray) -> np.ndarray:
@@ -111,7 +112,9 @@ def check_route(cfg, x64, w_r64, bias64, res, report: dict):
 
 
 def check_dispatch(cfg, res):
-    dp = O.dispatch(res["idx"], cfg.E, cfg.capacity)
+    """The oracle's dispatch on the GPU's own routing (selection and logits), bit-exact."""
+    dp = O.dispatch(res["idx"], cfg.E, cfg.capacity, cfg.priority, cfg.overflow,
+                    res["logits"].astype(np.float64))
     assert np.array_equal(res["counts"], dp["counts"]), "counts differ"
     assert np.array_equal(res["offsets"], dp["offsets"]), "offsets differ"
     R = int(dp["offsets"][-1])
@@ -127,6 +130,12 @@ def check_output(cfg, x64, z_o, res, fetch, shared, tokens: Optional[np.ndarray]
     idx = res["idx"]
     keep = res["inv"] >= 0
     w_o = O.topk_weights(z_o, idx, cfg.weights)
+    # the expert that computed each kept slot: the segment its row lies in (re-routing
+    # can move a slot off the router's choice; it keeps its weight)
+    seg = np.searchsorted(res["offsets"], np.maximum(res["inv"], 0), side="right") - 1
+    if cfg.overflow == "drop":
+        assert np.array_equal(seg[keep], idx[keep]), "a kept slot left its expert"
+    idx = np.where(keep, seg, idx)
     sel = np.arange(cfg.T) if tokens is None else np.asarray(tokens)
     ref = O.routed_output(x64[sel], idx[sel], w_o[sel], keep[sel], cfg.act, fetch, shared)
     got = res["out"][sel]

@@ -82,16 +82,25 @@ def test_route_validation(lib):
 
 
 def test_dispatch_validation(lib):
-    need = lib.moe_dispatch_workspace_bytes(1000, 16)
+    need = lib.moe_dispatch_workspace_bytes(1000, 16, 2)
     assert need >= 2 * 4 * 16 * 4
-    assert lib.moe_dispatch_workspace_bytes(1000, 16) == need       # pure
-    args = [16, 1000, 16, 2, 0, 16, 16, 16, 16, 16, 16, need, None]
-    bad_k = list(args); bad_k[3] = 17
-    assert lib.moe_dispatch(*bad_k) == 1
-    bad_ws = list(args); bad_ws[11] = need - 1
-    assert lib.moe_dispatch(*bad_ws) == 3
-    nul = list(args); nul[5] = None
-    assert lib.moe_dispatch(*nul) == 1
+    assert lib.moe_dispatch_workspace_bytes(1000, 16, 2) == need       # pure
+    assert lib.moe_dispatch_workspace_bytes(1000, 16, 4) > need        # slot-major tables grow with k
+    # idx, logits, T, E, k, capacity, priority, overflow, counts, offsets, perm, inv, nd, ws, ws_bytes, stream
+    args = [16, None, 1000, 16, 2, 0, 0, 0, 16, 16, 16, 16, 16, 16, need, None]
+    def call(**kw):
+        a = list(args)
+        pos = dict(logits=1, k=4, capacity=5, priority=6, overflow=7, perm=10, ws_bytes=14)
+        for n, v in kw.items():
+            a[pos[n]] = v
+        return lib.moe_dispatch(*a)
+    assert call(k=17) == 1
+    assert call(ws_bytes=need - 1) == 3
+    assert call(perm=None) == 1
+    assert call(priority=2) == 1
+    assert call(overflow=3) == 1
+    assert call(capacity=10, overflow=1) == 1                          # re-route needs logits
+    assert b"logits" in lib.moe_last_error()
 
 
 def test_ffn_validation(lib):
@@ -134,6 +143,11 @@ def test_layer_validation_and_workspace(lib):
     a.s_gate = 256                                  # shared expert without s_down
     assert lib.moe_layer_forward(C.byref(a), None) == 1
     a.s_gate = None
+    a.priority = 2
+    assert lib.moe_layer_forward(C.byref(a), None) == 1
+    a.priority, a.overflow = 1, 5
+    assert lib.moe_layer_forward(C.byref(a), None) == 1
+    a.overflow = 1
     a.d = 4000
     assert lib.moe_layer_forward(C.byref(a), None) == 2
     a.d = 4096

@@ -46,6 +46,14 @@ SMALL = {
                                       dtype="bf16", shared=True, bias_var=0.5, weights="softmax"),
     "f32-softmax-weights-k1": MoEConfig("f32-sw", 28, T=129, d=64, E=8, k=1, F=128, act="gelu", dtype="f32",
                                         weights="softmax"),
+    # capacity policies: first choices before second choices; overflow to the next-best expert
+    "bf16-capacity-slot-major": MoEConfig("bf16-cs", 31, T=400, d=256, E=8, k=2, F=256, act="swiglu",
+                                          dtype="bf16", capacity=60, bias_var=1.0, priority="slot"),
+    "bf16-capacity-reroute": MoEConfig("bf16-cr", 32, T=400, d=256, E=8, k=2, F=256, act="swiglu",
+                                       dtype="bf16", capacity=60, bias_var=1.0, overflow="reroute"),
+    "f32-reroute-slot-shared": MoEConfig("f32-rs", 33, T=150, d=64, E=6, k=2, F=128, act="swiglu", dtype="f32",
+                                         shared=True, capacity=30, bias_var=0.5, priority="slot",
+                                         overflow="reroute"),
 }
 
 
@@ -146,6 +154,29 @@ def test_route_shapes(T, d, E, k):
     say(f"[ok] route {cfg.name}: {rep}")
 
 
+@pytest.mark.parametrize("T,E,k,C", [(1, 4, 2, 1), (37, 5, 2, 4), (300, 8, 2, 40), (600, 16, 3, 70),
+                                     (129, 64, 6, 9), (200, 32, 10, 50), (513, 6, 1, 50), (40, 1000, 300, 8)])
+def test_dispatch_policies(T, E, k, C):
+    """moe_dispatch alone, every priority x overflow pair, bit-exact against the oracle
+    (skewed logits so capacity binds; multi-block and single-block passes; k > 8)."""
+    g = torch.Generator().manual_seed(1000 + T + E + k)
+    z = (torch.randn(T, E, generator=g) + torch.linspace(2.0, 0.0, E)).float()
+    idx = torch.as_tensor(O.select_topk(z.numpy().astype(np.float64), k), dtype=torch.int32)
+    zd, idxd = z.to(DEV), idx.to(DEV)
+    for pr in ("token", "slot"):
+        for ov in ("drop", "reroute"):
+            say(f"[case] dispatch T={T} E={E} k={k} C={C} {pr} {ov}")
+            dp = B.dispatch(idxd, E, C, pr, ov, zd)
+            torch.cuda.synchronize()
+            o = O.dispatch(idx.numpy(), E, C, pr, ov, z.numpy().astype(np.float64))
+            R = int(o["offsets"][-1])
+            assert np.array_equal(dp.counts.cpu().numpy(), o["counts"])
+            assert np.array_equal(dp.offsets.cpu().numpy(), o["offsets"])
+            assert np.array_equal(dp.perm.cpu().numpy()[:R], o["perm"])
+            assert np.array_equal(dp.inv.cpu().numpy(), o["inv"])
+            assert int(dp.n_dropped.item()) == o["n_dropped"]
+
+
 def test_stage_entry_points():
     """The four stage calls used one by one, each against the oracle."""
     cfg = MoEConfig("stages", 26, T=300, d=256, E=8, k=2, F=320, act="swiglu", dtype="bf16",
@@ -214,12 +245,15 @@ def test_empty_batch_is_noop():
 
 
 # ---- the five workloads at full size (routing on every token, outputs sampled) ----
-SAMPLES = {1: None, 2: 8, 3: 10, 4: 12, 5: None}
+SAMPLES = {1: None, 2: 8, 3: 10, 4: 12, 5: None, "4-slot-reroute": 12}
+FULL = {2: CONFIGS[2], 3: CONFIGS[3], 4: CONFIGS[4], 5: CONFIGS[5],
+        # the capacity workload with first choices first and overflow re-routed
+        "4-slot-reroute": CONFIGS[4].scaled(name="capacity-e16-slot-reroute", priority="slot", overflow="reroute")}
 
 
-@pytest.mark.parametrize("num", [2, 3, 4, 5])
+@pytest.mark.parametrize("num", list(FULL))
 def test_workload_full_size(num):
-    cfg = CONFIGS[num]
+    cfg = FULL[num]
     say(f"[case] full size {cfg.label}: generating inputs")
     inp = synth.make_inputs(cfg, DEV)
     torch.cuda.synchronize()
@@ -236,7 +270,7 @@ def test_workload_full_size(num):
     n = SAMPLES[num]
     tokens = None
     if n is not None:
-        rng = np.random.default_rng(num)
+        rng = np.random.default_rng(cfg.seed)
         tokens = np.sort(rng.choice(np.nonzero(~flip)[0], size=n, replace=False))
     check_output(cfg, x64, z_o, res, expert_fetcher(cfg, inp), shared_weights(inp), tokens, rep)
     rep["n_dropped"] = res["n_dropped"]
