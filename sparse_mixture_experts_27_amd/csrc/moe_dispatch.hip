@@ -285,7 +285,8 @@ size_t reroute_lds_bytes(int64_t T, int E, int k, bool slot_major, RerouteLds& c
   cfg.chunk = chunk;
   cfg.stage_e = E;
   cfg.stage_k = k;
-  cfg.tcache = slot_major && stage + tc <= 140 * 1024;
+  cfg.tcache = stage + tc <= 140 * 1024;
+  (void)slot_major;
   return stage + (cfg.tcache ? tc : 0);
 }
 
@@ -350,52 +351,134 @@ __global__ __launch_bounds__(64) void dispatch_reroute_kernel(
       if (t >= 0) kst[f] = idx[t * k + f % k];
     }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    while (mask) {                                    // lowest lane first = priority order
-      const int src = __builtin_ctzll(mask);
-      mask &= mask - 1;
-      const int32_t sl = __builtin_amdgcn_readlane(slot, src);
-      const int64_t t = __builtin_amdgcn_readlane(tok, src);
-      const int j = __builtin_amdgcn_readlane(jj, src);
-      if (m.slot_major || t != cur_t) {               // flags of a new token: its top-k ...
-        cur_t = t;
-        for (int e = lane; e < E; e += 64) used[e] = 0;
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        for (int q = lane; q < k; q += 64) {
-          const int32_t eq = kst[src * k + q];
-          if (static_cast<uint32_t>(eq) < static_cast<uint32_t>(E)) used[eq] = 1;
-          // ... and, in slot-major order, the targets of its earlier slot positions
-          if (m.slot_major && q < j) {
-            const int32_t tg = lc.tcache ? tcache[t * k + q]
-                                         : __builtin_amdgcn_raw_buffer_load_b32(
-                                               trs, static_cast<int>((t * k + q) * 4), 0, 1 /* glc: past L1 */);
-            if (tg >= 0) used[tg] = 1;
+    // Decisions.  Fast path (target copy in LDS, E*k <= 8192): every pending slot picks
+    // its best expert against the current room and its token's experts so far (top-k and
+    // the targets of its earlier slots, final for slots of earlier chunks).  A pick still
+    // open at the slot's turn is the greedy choice: room only shrinks and a token's
+    // experts only grow, so the candidates at its turn are a subset of those it saw (and a
+    // slot that saw none has none).  In priority order, a pick is still open if fewer
+    // earlier picks of this run chose the same expert than it has room, and no earlier
+    // slot of the same token in this run chose it.  The run up to the first pick that is
+    // not open is applied at once (ranks counted across lanes); the rest pick again.
+    // Slow path: one slot at a time with a wave-wide search.
+    const bool fast = lc.tcache && E * k <= 8192;
+    while (mask) {
+      if (fast) {
+        int32_t pick = -1;
+        const bool mine = (mask >> lane) & 1;
+        if (mine) {
+          uint32_t bhi = 0, blo = 0;
+          for (int e = 0; e < E; ++e) {
+            if (room[e] <= 0) continue;
+            bool excl = false;
+            for (int q = 0; q < k; ++q) {
+              excl |= kst[lane * k + q] == e;
+              if (q < jj) excl |= tcache[tok * k + q] == e;
+            }
+            if (excl) continue;
+            const uint32_t hi = dp_ordered_key(zst[lane * E + e]);
+            const uint32_t lo = 0xffffffffu - static_cast<uint32_t>(e);
+            if (hi > bhi || (hi == bhi && lo > blo)) { bhi = hi; blo = lo; }
+          }
+          pick = bhi != 0 ? static_cast<int32_t>(0xffffffffu - blo) : -1;
+        }
+        // rank among earlier picks of the same expert, and token clashes (readlane takes a
+        // uniform lane index, so every lane walks all 64)
+        int32_t before = 0;
+        bool clash = false;
+        for (int i2 = 0; i2 < 64; ++i2) {
+          if (!((mask >> i2) & 1)) continue;          // uniform
+          const int32_t pi = __builtin_amdgcn_readlane(pick, i2);
+          const int32_t ti = __builtin_amdgcn_readlane(tok, i2);
+          if (pi < 0 || pi != pick) continue;
+          if (i2 < lane) {
+            ++before;
+            clash |= ti == tok;
           }
         }
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      }
-      uint32_t bhi = 0, blo = 0;
-      for (int e = lane; e < E; e += 64) {
-        if (room[e] <= 0 || used[e]) continue;
-        const uint32_t hi = dp_ordered_key(zst[src * E + e]);
-        const uint32_t lo = 0xffffffffu - static_cast<uint32_t>(e);
-        if (hi > bhi || (hi == bhi && lo > blo)) { bhi = hi; blo = lo; }
-      }
-      wave_key_max(bhi, blo);
-      if (bhi != 0) {                                 // an expert with room was found
-        const int32_t e = static_cast<int32_t>(0xffffffffu - blo);
-        const int32_t a = arr[e];
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        if (lane == 0) {
-          room[e] = room[e] - 1;
-          arr[e] = a + 1;
-          used[e] = 1;
-          if (lc.tcache) tcache[sl] = e;
-          target[sl] = e;
-          arrival[sl] = a;
+        const bool closed = mine && pick >= 0 && (before >= room[pick] || clash);
+        const uint64_t cmask = __ballot(closed);
+        const uint64_t done = cmask ? (mask & ((uint64_t{1} << __builtin_ctzll(cmask)) - 1)) : mask;
+        if (!done) {                                  // the first slot is not open: decide it alone
+          goto one_slot;
         }
-        ++moved;
-        if (m.slot_major && !lc.tcache) __builtin_amdgcn_s_waitcnt(0);   // before any read-back
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        {
+          const bool take = ((done >> lane) & 1) && pick >= 0;
+          // the last taker of an expert (no later taker in the run) updates its counters
+          int32_t later = 0;
+          for (int i2 = 0; i2 < 64; ++i2) {           // uniform lane index for readlane
+            if (!((done >> i2) & 1)) continue;
+            const int32_t pi = __builtin_amdgcn_readlane(pick, i2);
+            later += (i2 > lane && pi == pick) ? 1 : 0;
+          }
+          int32_t a0 = 0, r0 = 0;
+          if (take) {
+            a0 = arr[pick];
+            r0 = room[pick];
+          }
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          if (take) {
+            target[slot] = pick;
+            arrival[slot] = a0 + before;
+            tcache[slot] = pick;
+            if (later == 0) {
+              arr[pick] = a0 + before + 1;
+              room[pick] = r0 - (before + 1);
+            }
+          }
+          moved += static_cast<int32_t>(__builtin_popcountll(__ballot(take)));
+          mask &= ~done;
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          continue;
+        }
+      }
+    one_slot: {
+        const int src = __builtin_ctzll(mask);
+        const int32_t sl = __builtin_amdgcn_readlane(slot, src);
+        const int64_t t = __builtin_amdgcn_readlane(tok, src);
+        const int j = __builtin_amdgcn_readlane(jj, src);
+        if (m.slot_major || t != cur_t || fast) {     // flags of the token: its top-k ...
+          cur_t = t;
+          for (int e = lane; e < E; e += 64) used[e] = 0;
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          for (int q = lane; q < k; q += 64) {
+            const int32_t eq = kst[src * k + q];
+            if (static_cast<uint32_t>(eq) < static_cast<uint32_t>(E)) used[eq] = 1;
+            // ... and the targets of its earlier slots
+            if (q < j && (m.slot_major || fast)) {
+              const int32_t tg = lc.tcache ? tcache[t * k + q]
+                                           : __builtin_amdgcn_raw_buffer_load_b32(
+                                                 trs, static_cast<int>((t * k + q) * 4), 0, 1 /* glc: past L1 */);
+              if (tg >= 0) used[tg] = 1;
+            }
+          }
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        }
+        uint32_t bhi = 0, blo = 0;
+        for (int ee = lane; ee < E; ee += 64) {
+          if (room[ee] <= 0 || used[ee]) continue;
+          const uint32_t hi = dp_ordered_key(zst[src * E + ee]);
+          const uint32_t lo = 0xffffffffu - static_cast<uint32_t>(ee);
+          if (hi > bhi || (hi == bhi && lo > blo)) { bhi = hi; blo = lo; }
+        }
+        wave_key_max(bhi, blo);
+        const int32_t e = bhi != 0 ? static_cast<int32_t>(0xffffffffu - blo) : -1;
+        mask &= mask - 1;
+        if (e >= 0) {                                 // an expert with room
+          const int32_t a = arr[e];
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          if (lane == 0) {
+            room[e] = room[e] - 1;
+            arr[e] = a + 1;
+            used[e] = 1;
+            if (lc.tcache) tcache[sl] = e;
+            target[sl] = e;
+            arrival[sl] = a;
+          }
+          ++moved;
+          if (!lc.tcache) __builtin_amdgcn_s_waitcnt(0);   // before any read-back
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        }
       }
     }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);          // staging area reused by the next chunk
