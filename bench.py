@@ -35,7 +35,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2, help="workload number 1-5 (default 2: prefill, E=64)")
+    ap.add_argument("--config", type=int, default=2, help="workload number 1-7 (default 2: prefill, E=64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-experts", type=int, default=1024,
                     help="experts whose rows the CPU oracle computes for its timed sample")

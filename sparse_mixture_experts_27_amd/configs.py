@@ -1,4 +1,4 @@
-"""The five MoE-layer workloads (shapes of the layers the source pages describe).
+"""The MoE-layer workloads (shapes of the layers the source pages describe).
 
 Sizes follow the pages' running examples: 64 experts with top-2 ([mlqm] §2.2, [wmrh]
 §2.2), hidden width 4096 ([mlqm] §3.1), 16 routed experts plus one shared expert
@@ -49,4 +49,11 @@ CONFIGS = {
     4: MoEConfig("capacity-e16", 4, T=1024, d=4096, E=16, k=2, F=14336, act="swiglu",
                  dtype="bf16", capacity=128, bias_var=1.0),
     5: MoEConfig("decode-e64", 5, T=16, d=4096, E=64, k=2, F=14336, act="swiglu", dtype="bf16"),
+    # wider routing shapes: 384 routed experts, 6 per token, one shared expert ([200B-5]
+    # closing section's recent-model example) and 128 experts top-2 (the MoE-128 option of
+    # the expert-count comparison on the first page); the pages give no widths for them,
+    # so d and F stay those of the other workloads
+    6: MoEConfig("wide-e384-top6-shared", 6, T=4096, d=4096, E=384, k=6, F=14336, act="swiglu", dtype="bf16",
+                 shared=True),
+    7: MoEConfig("wide-e128-top2", 7, T=4096, d=4096, E=128, k=2, F=14336, act="swiglu", dtype="bf16"),
 }

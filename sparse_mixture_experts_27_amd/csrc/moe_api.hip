@@ -166,7 +166,7 @@ moe_status_t moe_dispatch(const int32_t* topk_idx, const float* logits, int64_t 
 size_t moe_expert_ffn_workspace_bytes(int64_t max_rows, int32_t G, int64_t d, int64_t F, moe_act_t act,
                                       moe_dtype_t dt) {
   if (max_rows < 0 || G < 1 || d < 1 || F < 1) return 0;
-  return ffn_plan(max_rows, G, false, d, F, act, dt).ws_bytes;
+  return ffn_plan(max_rows, G, 0, d, F, act, dt).ws_bytes;
 }
 
 moe_status_t moe_expert_ffn(const void* x, const int32_t* perm, int32_t k, const int32_t* offsets, int32_t G,
@@ -176,7 +176,7 @@ moe_status_t moe_expert_ffn(const void* x, const int32_t* perm, int32_t k, const
   g_last_error[0] = 0;
   if (moe_status_t st = check_ffn_args(x, offsets, G, max_rows, d, F, act, dt, w_gate, w_up, w_down, y)) return st;
   if (perm && k < 1) return fail(MOE_EINVAL, "k must be >= 1 when perm is given");
-  const FfnPlan plan = ffn_plan(max_rows, G, false, d, F, act, dt);
+  const FfnPlan plan = ffn_plan(max_rows, G, 0, d, F, act, dt);
   if (!ws || ws_bytes < plan.ws_bytes)
     return fail(MOE_EWORKSPACE, "expert FFN needs %zu workspace bytes, got %zu", plan.ws_bytes, ws_bytes);
   FfnProblem p{};
@@ -217,7 +217,7 @@ static size_t layer_layout(const moe_layer_args_t* a, bool carve, WsCarver& c, i
   const int64_t T = a->T;
   const bool shared = a->s_gate != nullptr;
   const int64_t max_rows = T * a->k + (shared ? T : 0);
-  *plan = ffn_plan(max_rows, a->E, shared, a->d, a->F, a->act, a->dt, a->capacity);
+  *plan = ffn_plan(max_rows, a->E, shared ? T : 0, a->d, a->F, a->act, a->dt, a->capacity);
   float* lg = c.take<float>(static_cast<size_t>(T) * a->E);
   int32_t* ix = c.take<int32_t>(static_cast<size_t>(T) * a->k);
   float* tw = c.take<float>(static_cast<size_t>(T) * a->k);

@@ -79,8 +79,9 @@ struct FfnPlan {
   int64_t max_mtiles;
   size_t ws_bytes;
 };
-// capacity: per-group row limit if known (0 = unknown); only tunes the tile height.
-FfnPlan ffn_plan(int64_t max_rows, int G, bool has_shared, int64_t d, int64_t F, int act, int dt,
+// shared_rows: rows of the shared group inside max_rows (0 = none); capacity: per-group
+// row limit if known (0 = unknown).  Both only tune the tile height.
+FfnPlan ffn_plan(int64_t max_rows, int G, int64_t shared_rows, int64_t d, int64_t F, int act, int dt,
                  int64_t capacity = 0);
 // y: [splits][max_rows][d] fp32 partial sums when plan.splits > 1 and reduce_splits is
 // false; otherwise [max_rows][d] final.

@@ -590,21 +590,23 @@ void launch_bf16_gemm(int bm, int nw, int64_t grid, const GemmArgs& g, hipStream
 
 }  // namespace
 
-// M-tile height: the smallest of 32/64/128/256 rows that holds a typical group in one
-// tile, so each expert's weights stream once.  The rows per group are only known on the
-// device; the host estimate is the capacity when one is set, else 1.6x the mean load
-// (plus a margin for small loads).
-FfnPlan ffn_plan(int64_t max_rows, int G, bool has_shared, int64_t d, int64_t F, int act, int dt,
+// M-tile height: the smallest of 32/64/128/256 rows that holds a typical routed group in
+// one tile, so each expert's weights stream once.  The rows per group are only known on
+// the device; the host estimate is the capacity when one is set, else 1.6x the mean load
+// (plus a margin for small loads).  A shared group (T rows) does not raise it: its M-tiles
+// are adjacent in the schedule and share its weights in L2, while routed experts are the
+// bulk of the weight bytes.
+FfnPlan ffn_plan(int64_t max_rows, int G, int64_t shared_rows, int64_t d, int64_t F, int act, int dt,
                  int64_t capacity) {
   FfnPlan pl{};
   (void)act;
+  const bool has_shared = shared_rows > 0;
   const int Gt = G + (has_shared ? 1 : 0);
   if (dt == MOE_BF16) {
-    const int64_t routed = max_rows;
+    const int64_t routed = max_rows - (has_shared ? shared_rows : 0);
     double est = 1.6 * static_cast<double>(routed) / (G > 0 ? G : 1) + 16.0;
     if (capacity > 0 && static_cast<double>(capacity) < est) est = static_cast<double>(capacity);
     pl.bm = est <= 32 ? 32 : est <= 64 ? 64 : est <= 128 ? 128 : BM;
-    if (has_shared) pl.bm = BM;
     // tuning override of the tile height (32, 64, 128 or 256 rows)
     if (const char* o = getenv("MOE_TILE_ROWS")) {
       const int v = atoi(o);

@@ -245,8 +245,8 @@ def test_empty_batch_is_noop():
 
 
 # ---- the five workloads at full size (routing on every token, outputs sampled) ----
-SAMPLES = {1: None, 2: 8, 3: 10, 4: 12, 5: None, "4-slot-reroute": 12}
-FULL = {2: CONFIGS[2], 3: CONFIGS[3], 4: CONFIGS[4], 5: CONFIGS[5],
+SAMPLES = {1: None, 2: 8, 3: 10, 4: 12, 5: None, "4-slot-reroute": 12, 6: 4, 7: 8}
+FULL = {2: CONFIGS[2], 3: CONFIGS[3], 4: CONFIGS[4], 5: CONFIGS[5], 6: CONFIGS[6], 7: CONFIGS[7],
         # the capacity workload with first choices first and overflow re-routed
         "4-slot-reroute": CONFIGS[4].scaled(name="capacity-e16-slot-reroute", priority="slot", overflow="reroute")}
 
