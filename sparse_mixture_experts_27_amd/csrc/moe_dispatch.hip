@@ -17,10 +17,12 @@
 //               the block + earlier lanes of the wave; kept slots go to
 //               perm[offsets[e] + rank], inv gets the row or -1
 // A batch of at most 256 virtual tokens runs all three in one workgroup.
-// Re-routing adds two passes: one wave walks the overflowed slots in priority order and
-// gives each the best expert (by logit, lowest index on ties) outside the token's top-k
-// and earlier re-routes that still has room; then every slot's row is rebuilt, with
-// the router-chosen rows of an expert first and its re-routed arrivals after them.
+// Re-routing adds passes: the overflowed slots are listed in priority order (one
+// workgroup), one wave walks them and gives each the best expert (by logit, lowest index
+// on ties) outside the token's top-k and earlier re-routes that still has room (with at
+// most 64 experts and 16384 tokens all its state is in registers and LDS; otherwise a
+// general walk over the priority positions), then every slot's row is rebuilt, with the
+// router-chosen rows of an expert first and its re-routed arrivals after them.
 #include "moe_common.h"
 
 namespace moe {
@@ -509,6 +511,175 @@ __global__ __launch_bounds__(64) void dispatch_reroute_kernel(
   if (lane == 0) *n_dropped = dropped1 - moved;
 }
 
+// ---- re-routing with at most 64 experts --------------------------------------------
+// Overflow list: the slots that overflowed (a valid expert, no row after the capacity
+// pass) in priority order, from one workgroup that walks the priority positions in
+// blocks of 1024; every slot without a row gets target -1 here.
+__global__ __launch_bounds__(1024) void reroute_list_kernel(const int32_t* __restrict__ idx,
+                                                            const int32_t* __restrict__ inv, SlotMap m, int E,
+                                                            int32_t* __restrict__ target,
+                                                            int32_t* __restrict__ ovl, int32_t* __restrict__ n_over) {
+  __shared__ int32_t wsum[16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t nslots = m.T * m.k;
+  int32_t base = 0;
+  for (int64_t p0 = 0; p0 < nslots; p0 += 1024) {
+    const int64_t p = p0 + threadIdx.x;
+    bool over = false;
+    int32_t slot = 0;
+    if (p < nslots) {
+      slot = static_cast<int32_t>(m.slot_major ? (p % m.T) * m.k + p / m.T : p);
+      if (inv[slot] < 0) {
+        target[slot] = -1;
+        over = static_cast<uint32_t>(idx[slot]) < static_cast<uint32_t>(E);
+      }
+    }
+    const uint64_t b = __ballot(over);
+    if (lane == 0) wsum[wave] = __builtin_popcountll(b);
+    __syncthreads();
+    int32_t before = base, total = base;
+    for (int w = 0; w < 16; ++w) {
+      before += w < wave ? wsum[w] : 0;
+      total += wsum[w];
+    }
+    if (over) ovl[before + __builtin_popcountll(b & ((uint64_t{1} << lane) - 1))] = slot;
+    base = total;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *n_over = base;
+}
+
+// One wave walks the overflow list in chunks of 64 entries (lane i holds entry c+i).  Expert
+// e's room and re-routed arrivals live in lane e; each lane holds its token's logit row in
+// registers and a mask of the experts the token may not take (its top-k, plus an LDS mask
+// per token of the experts its earlier slots were re-routed to).  Every pending lane picks
+// the best expert with room outside that mask (highest logit, lowest index on ties).  A
+// pick is still the greedy choice at the lane's turn if fewer earlier lanes of the run
+// picked the same expert than it has room and no earlier lane of the same token picked it
+// (room only shrinks and a token's excluded set only grows), so the run up to the first
+// pick that fails this is applied at once and the rest pick again; the first pending lane
+// always succeeds, so every round makes progress.  Same-token entries are adjacent in
+// token-major order (checked k-1 lanes back); in slot-major order a run stops where the
+// slot position changes, and within one slot position the tokens are distinct.
+__global__ __launch_bounds__(64) void reroute64_kernel(const int32_t* __restrict__ idx,
+                                                       const float* __restrict__ logits, SlotMap m, int E,
+                                                       int64_t capacity, const int32_t* __restrict__ ovl,
+                                                       const int32_t* __restrict__ n_over_p,
+                                                       int32_t* __restrict__ offsets, int32_t* __restrict__ off1,
+                                                       int32_t* __restrict__ target, int32_t* __restrict__ arrival,
+                                                       int32_t* __restrict__ n_dropped) {
+  extern __shared__ uint64_t tused[];                   // [T]: experts the token's re-routes took
+  const int lane = threadIdx.x;
+  const int k = m.k;
+  for (int64_t t = lane; t < m.T; t += 64) tused[t] = 0;
+  int32_t kept = 0, room = 0, arr = 0;
+  if (lane < E) {
+    const int32_t o0 = offsets[lane], o1 = offsets[lane + 1];
+    off1[lane] = o0;
+    kept = o1 - o0;
+    room = static_cast<int32_t>(capacity) - kept;
+  }
+  if (lane == 0) off1[E] = offsets[E];
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  const uint64_t emask = E >= 64 ? ~uint64_t{0} : (uint64_t{1} << E) - 1;
+  const uint64_t below = (uint64_t{1} << lane) - 1;
+  const int32_t n_over = *n_over_p;
+  const int32_t dropped1 = *n_dropped;
+  int32_t moved = 0;
+  for (int32_t c0 = 0; c0 < n_over; c0 += 64) {
+    const bool has = c0 + lane < n_over;
+    const int32_t slot = has ? ovl[c0 + lane] : 0;
+    const int32_t tok = slot / k, jj = slot - (slot / k) * k;
+    float z[64];
+    uint64_t tk = 0;
+#pragma unroll
+    for (int e = 0; e < 64; ++e) z[e] = (has && e < E) ? logits[static_cast<int64_t>(tok) * E + e] : 0.f;
+    for (int q = 0; q < k; ++q) {
+      const int32_t eq = has ? idx[static_cast<int64_t>(tok) * k + q] : -1;
+      if (static_cast<uint32_t>(eq) < static_cast<uint32_t>(E)) tk |= uint64_t{1} << eq;
+    }
+    uint64_t pending = __ballot(has);
+    while (pending) {
+      const uint64_t avail = __ballot(lane < E && room > 0) & emask;
+      const bool mine = (pending >> lane) & 1;
+      int32_t pick = -1;
+      if (mine) {
+        const uint64_t cand = avail & ~(tk | tused[tok]);
+        float best = 0.f;
+#pragma unroll
+        for (int e = 0; e < 64; ++e) {
+          if ((cand >> e) & 1) {
+            if (pick < 0 || z[e] > best) {
+              best = z[e];
+              pick = e;
+            }
+          }
+        }
+      }
+      // rank among earlier lanes of the run with the same pick, per distinct pick
+      const int first = __builtin_ctzll(pending);
+      int32_t before = 0;
+      uint64_t rem = __ballot(mine && pick >= 0);
+      while (rem) {
+        const int32_t e = __builtin_amdgcn_readlane(pick, __builtin_ctzll(rem));
+        const uint64_t me = __ballot(mine && pick == e);
+        if (mine && pick == e) before = __builtin_popcountll(me & below);
+        rem &= ~me;
+      }
+      bool clash = false;
+      if (m.slot_major) {
+        clash = jj != __builtin_amdgcn_readlane(jj, first);   // another slot position: next round
+      } else {
+        for (int d = 1; d < k && d < 64; ++d) {
+          const int32_t tu = __shfl_up(tok, d), pu = __shfl_up(pick, d);
+          clash |= lane >= d && ((pending >> (lane - d)) & 1) && tu == tok && pu == pick;
+        }
+      }
+      const int32_t room_p = __shfl(room, pick < 0 ? 0 : pick);
+      const bool closed = mine && pick >= 0 && (before >= room_p || clash);
+      const uint64_t cmask = __ballot(closed);
+      // (the first pending lane is never closed - its pick has room and nothing before it
+      // in the run - so it is always done and every round makes progress)
+      const uint64_t done = (cmask ? (pending & ((uint64_t{1} << __builtin_ctzll(cmask)) - 1)) : pending) |
+                            (pending & (~pending + 1));
+      const bool take = ((done >> lane) & 1) && pick >= 0;
+      const int32_t arr_p = __shfl(arr, pick < 0 ? 0 : pick);
+      if (take) {
+        target[slot] = pick;
+        arrival[slot] = arr_p + before;
+        atomicOr(reinterpret_cast<unsigned long long*>(&tused[tok]), 1ull << pick);
+      }
+      // counters of the experts taken in this run
+      uint64_t tm = __ballot(take);
+      moved += __builtin_popcountll(tm);
+      while (tm) {
+        const int32_t e = __builtin_amdgcn_readlane(pick, __builtin_ctzll(tm));
+        const uint64_t me = __ballot(take && pick == e);
+        const int32_t n = __builtin_popcountll(me);
+        if (lane == e) {
+          room -= n;
+          arr += n;
+        }
+        tm &= ~me;
+      }
+      pending &= ~done;
+      // one wave's LDS accesses execute in issue order: the mask updates precede the next
+      // round's reads once the compiler keeps them in order
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    }
+  }
+  // new offsets: kept + arrivals, exclusive scan over experts (lane e holds expert e)
+  int32_t incl = lane < E ? kept + arr : 0;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t x = __shfl_up(incl, o);
+    if (lane >= o) incl += x;
+  }
+  if (lane < E) offsets[lane] = incl - (kept + arr);
+  if (lane == E - 1) offsets[E] = incl;
+  if (lane == 0) *n_dropped = dropped1 - moved;
+}
+
 // Rebuild rows after re-routing: a router-chosen kept slot keeps its rank inside its
 // expert; a re-routed slot goes after its new expert's router-chosen rows.
 __global__ __launch_bounds__(256) void dispatch_rebuild_kernel(
@@ -538,7 +709,7 @@ size_t dispatch_ws_bytes(int64_t T, int E, int k) {
   const int64_t nb = (T * k + DP_TOK - 1) / DP_TOK;
   return 2 * align_up(static_cast<size_t>(nb) * E * sizeof(int32_t), 256) +
          align_up(static_cast<size_t>(E + 1) * sizeof(int32_t), 256) +
-         2 * align_up(static_cast<size_t>(T) * k * sizeof(int32_t), 256);
+         3 * align_up(static_cast<size_t>(T) * k * sizeof(int32_t), 256) + align_up(sizeof(int32_t), 256);
 }
 
 moe_status_t launch_dispatch(const int32_t* topk_idx, const float* logits, int64_t T, int E, int k,
@@ -554,6 +725,8 @@ moe_status_t launch_dispatch(const int32_t* topk_idx, const float* logits, int64
   int32_t* off1 = c.take<int32_t>(static_cast<size_t>(E) + 1);
   int32_t* target = c.take<int32_t>(static_cast<size_t>(T) * k);
   int32_t* arrival = c.take<int32_t>(static_cast<size_t>(T) * k);
+  int32_t* ovl = c.take<int32_t>(static_cast<size_t>(T) * k);
+  int32_t* n_over = c.take<int32_t>(1);
   if (nb <= 1) {
     const SlotMap mg{nb == 0 ? 0 : T, k, m.slot_major};
     dispatch_small_kernel<<<1, 256, 0, s>>>(topk_idx, mg, E, capacity, counts, offsets, perm, inv, n_dropped);
@@ -569,13 +742,25 @@ moe_status_t launch_dispatch(const int32_t* topk_idx, const float* logits, int64
     if (moe_status_t st = check_launch("dispatch scatter kernel")) return st;
   }
   if (overflow != MOE_OVERFLOW_REROUTE || capacity <= 0 || T == 0) return MOE_OK;
+  const int64_t nslots = T * k;
+  if (E <= 64 && T <= 16384) {
+    reroute_list_kernel<<<1, 1024, 0, s>>>(topk_idx, inv, m, E, target, ovl, n_over);
+    if (moe_status_t st = check_launch("dispatch overflow-list kernel")) return st;
+    const size_t lds = static_cast<size_t>(T) * sizeof(uint64_t);
+    set_max_dynamic_smem(reinterpret_cast<const void*>(reroute64_kernel), lds);
+    reroute64_kernel<<<1, 64, lds, s>>>(topk_idx, logits, m, E, capacity, ovl, n_over, offsets, off1, target,
+                                        arrival, n_dropped);
+    if (moe_status_t st = check_launch("dispatch re-route kernel")) return st;
+    dispatch_rebuild_kernel<<<static_cast<unsigned>((nslots + 255) / 256), 256, 0, s>>>(
+        topk_idx, nslots, E, off1, offsets, target, arrival, perm, inv);
+    return check_launch("dispatch rebuild kernel");
+  }
   RerouteLds lc{};
   const size_t lds = reroute_lds_bytes(T, E, k, m.slot_major, lc);
   set_max_dynamic_smem(reinterpret_cast<const void*>(dispatch_reroute_kernel), lds);
   dispatch_reroute_kernel<<<1, 64, lds, s>>>(topk_idx, logits, m, E, capacity, lc, inv, offsets, off1, target,
                                              arrival, n_dropped);
   if (moe_status_t st = check_launch("dispatch re-route kernel")) return st;
-  const int64_t nslots = T * k;
   dispatch_rebuild_kernel<<<static_cast<unsigned>((nslots + 255) / 256), 256, 0, s>>>(
       topk_idx, nslots, E, off1, offsets, target, arrival, perm, inv);
   return check_launch("dispatch rebuild kernel");
