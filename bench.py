@@ -36,6 +36,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, help="workload number 1-7 (default 2: prefill, E=64)")
+    ap.add_argument("--priority", choices=("token", "slot"), default=None,
+                    help="capacity priority (default: the workload's, token-major)")
+    ap.add_argument("--overflow", choices=("drop", "reroute"), default=None,
+                    help="fate of a slot beyond capacity (default: the workload's, drop)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-experts", type=int, default=1024,
                     help="experts whose rows the CPU oracle computes for its timed sample")
@@ -137,8 +141,8 @@ def cpu_baseline(cfg, inp, L, n_exp):
     t0 = time.perf_counter()
     z = O.router_logits(x64, wr64, b64)
     idx = O.select_topk(z, cfg.k)
-    w = O.topk_weights(z, idx)
-    dp = O.dispatch(idx, cfg.E, cfg.capacity)
+    w = O.topk_weights(z, idx, cfg.weights)
+    dp = O.dispatch(idx, cfg.E, cfg.capacity, cfg.priority, cfg.overflow, z)
     out = np.zeros((cfg.T, cfg.d))
     t_oracle = time.perf_counter() - t0
     kept = np.diff(dp["offsets"])
@@ -160,6 +164,8 @@ def cpu_baseline(cfg, inp, L, n_exp):
     tokens_equiv = rows / cfg.k
     whole = len(experts) == int((kept > 0).sum())
     what = "the whole layer" if whole else f"{rows} of {int(kept.sum())} routed rows ({len(experts)} experts)"
+    if cfg.shared:
+        what += " (routed experts only: the shared expert is not timed)"
     return dict(value=round(tokens_equiv / t_oracle, 2), unit="tokens/s", cores=int(threads), kind="oracle",
                 sample=(f"{cfg.name}: routing + dispatch of all {cfg.T} tokens and FFN + combine of {what} "
                         f"(= {tokens_equiv:.0f} token-equivalents), float64 numpy, {t_oracle:.1f} s of oracle time"),
@@ -181,12 +187,15 @@ def main():
     from sparse_mixture_experts_27_amd.configs import CONFIGS
 
     cfg = CONFIGS[args.config]
+    if args.priority or args.overflow:
+        cfg = cfg.scaled(priority=args.priority or cfg.priority, overflow=args.overflow or cfg.overflow)
     B.lib()                                  # fail loudly if the HIP library is missing
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     inp = synth.make_inputs(cfg, dev)
     L = B.Layer(inp["w_r"], inp["w_gate"], inp["w_up"], inp["w_down"], cfg.k, act=cfg.act, bias=inp["bias"],
-                capacity=cfg.capacity, s_gate=inp["s_gate"], s_up=inp["s_up"], s_down=inp["s_down"])
+                capacity=cfg.capacity, s_gate=inp["s_gate"], s_up=inp["s_up"], s_down=inp["s_down"],
+                weights=cfg.weights, priority=cfg.priority, overflow=cfg.overflow)
     x = inp["x"]
     for _ in range(args.warmup):
         L(x)
@@ -233,7 +242,8 @@ def main():
         "dtype": cfg.dtype,
         "data": "synthetic (seeded N(0,1) hidden states, N(0,1/fan_in) random-init weights)",
         "config": {"workload": cfg.label, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k, "F": cfg.F,
-                   "act": cfg.act, "shared": cfg.shared, "capacity": cfg.capacity, "parallelism": "single-gpu"},
+                   "act": cfg.act, "shared": cfg.shared, "capacity": cfg.capacity, "priority": cfg.priority,
+                   "overflow": cfg.overflow, "parallelism": "single-gpu"},
         "roofline": roof,
         "layer_roofline": layer_roof,
         "down_roofline": down_roof,
