@@ -145,10 +145,30 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& p, int bm, TileInfo&
     if (static_cast<int64_t>(pre[mid]) * nts <= L) lo = mid; else hi = mid;
   }
   const int g = lo;
+  // Inside a group the tiles go in blocks of up to MB M-tiles: all N-tiles (and K splits)
+  // of one block, M fastest, then the next block.  The workgroups running at once on an
+  // XCD then share both the weights of a few N-tiles and the activation rows of a few
+  // M-tiles in its L2 (with M fastest over a whole large group, every round of N-tiles
+  // would re-read all of the group's activation rows).
   const int64_t local = L - static_cast<int64_t>(pre[g]) * nts;
   const int mt = pre[g + 1] - pre[g];
-  const int64_t j = local / mt;
-  const int m = static_cast<int>(local - j * mt);
+  constexpr int MB = 4;
+  const int A = mt < MB ? mt : MB;
+  const int nfull = mt / A;
+  const int64_t in_full = static_cast<int64_t>(nfull) * A * nts;
+  int64_t j;
+  int m;
+  if (local < in_full) {
+    const int64_t mb = local / (static_cast<int64_t>(A) * nts);
+    const int64_t r = local - mb * A * nts;
+    j = r / A;
+    m = static_cast<int>(mb * A + (r - j * A));
+  } else {                                    // the last, partial block
+    const int A2 = mt - nfull * A;
+    const int64_t r = local - in_full;
+    j = r / A2;
+    m = nfull * A + static_cast<int>(r - j * A2);
+  }
   ti.g = g;
   ti.ntile = static_cast<int>(j / p.splits);
   ti.split = static_cast<int>(j - static_cast<int64_t>(ti.ntile) * p.splits);
