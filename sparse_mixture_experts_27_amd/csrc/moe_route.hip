@@ -300,24 +300,43 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(
     f32x4 acc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int j0 = wave; j0 < nsteps; j0 += 4 * U) {
-      bf16x8 a[U], b[U][4];
+    // Batches of U K steps, double-buffered: the next batch's loads are issued before the
+    // current batch's MFMAs, so one memory latency covers the whole walk rather than one
+    // per batch.
+    bf16x8 a[2][U], b[2][U][4];
+    auto load = [&](int buf, int j0) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int j = j0 + 4 * u < nsteps ? j0 + 4 * u : j0;    // past the range: a repeated step, not used
-        a[u] = *reinterpret_cast<const bf16x8*>(xrow + j * 32);
+        a[buf][u] = *reinterpret_cast<const bf16x8*>(xrow + j * 32);
 #pragma unroll
         for (int nf = 0; nf < 4; ++nf)
-          b[u][nf] = *reinterpret_cast<const bf16x8*>(wrow + static_cast<int64_t>(nf < nfr ? nf : 0) * 16 * d + j * 32);
+          b[buf][u][nf] =
+              *reinterpret_cast<const bf16x8*>(wrow + static_cast<int64_t>(nf < nfr ? nf : 0) * 16 * d + j * 32);
       }
+    };
+    auto mul = [&](int buf, int j0) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (j0 + 4 * u < nsteps) {
 #pragma unroll
           for (int nf = 0; nf < 4; ++nf)
-            if (nf < nfr) acc[nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u][nf], acc[nf], 0, 0, 0);
+            if (nf < nfr) acc[nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[buf][u], b[buf][u][nf], acc[nf], 0, 0, 0);
         }
       }
+    };
+    int j0 = wave;
+    if (j0 < nsteps) load(0, j0);
+    while (j0 < nsteps) {
+      int jn = j0 + 4 * U;
+      if (jn < nsteps) load(1, jn);
+      mul(0, j0);
+      j0 = jn;
+      if (j0 >= nsteps) break;
+      jn = j0 + 4 * U;
+      if (jn < nsteps) load(0, jn);
+      mul(1, j0);
+      j0 = jn;
     }
     // C layout of the 16x16 MFMA: lane holds rows 4*(lane/16)+v, column lane%16
     __syncthreads();                         // previous pass's partials consumed
