@@ -4,7 +4,7 @@
 #include "moe_common.h"
 
 #include <mutex>
-#include <set>
+#include <map>
 #include <utility>
 
 namespace moe {
@@ -35,13 +35,18 @@ moe_status_t check_launch(const char* what) {
 }
 
 void set_max_dynamic_smem(const void* func, size_t bytes) {
+  // the attribute is a per-device cap: raise it whenever a launch needs more than any
+  // earlier one on this device (a later, larger problem must not inherit a smaller cap)
   static std::mutex mu;
-  static std::set<std::pair<int, const void*>> done;
+  static std::map<std::pair<int, const void*>, size_t> cap;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return;
   std::lock_guard<std::mutex> lk(mu);
-  if (done.insert({dev, func}).second)
-    (void)hipFuncSetAttribute(func, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+  size_t& c = cap[{dev, func}];
+  if (bytes > c) {
+    if (hipFuncSetAttribute(func, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes)) == hipSuccess)
+      c = bytes;
+  }
 }
 
 namespace {
