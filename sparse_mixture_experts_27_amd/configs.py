@@ -57,3 +57,6 @@ CONFIGS = {
                  shared=True),
     7: MoEConfig("wide-e128-top2", 7, T=4096, d=4096, E=128, k=2, F=14336, act="swiglu", dtype="bf16"),
 }
+
+# the workloads by name
+BY_NAME = {c.name: c for c in CONFIGS.values()}
