@@ -40,6 +40,9 @@ def parse():
                     help="capacity priority (default: the workload's, token-major)")
     ap.add_argument("--overflow", choices=("drop", "reroute"), default=None,
                     help="fate of a slot beyond capacity (default: the workload's, drop)")
+    ap.add_argument("--layout", choices=("packed", "linear"), default="packed",
+                    help="storage order of the expert weights in HBM (default packed: reordered once "
+                         "at load time by moe_pack_weights; linear: the nn.Linear layout as given)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-experts", type=int, default=1024,
                     help="experts whose rows the CPU oracle computes for its timed sample")
@@ -59,15 +62,17 @@ def source_digest(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(cfg_name: str):
+def measured_traffic(cfg_name: str, layout: str):
     """HBM bytes per launch of the gate/up GEMM from the committed counter summary, or None
-    when there is none for this workload or the GEMM source changed since it was taken."""
+    when there is none for this workload and weight layout or the GEMM source changed
+    since it was taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("workload") != cfg_name or t.get("ffn_source_sha256_16") != source_digest(FFN_SOURCE):
+    if (t.get("workload") != cfg_name or t.get("weight_layout") != layout
+            or t.get("ffn_source_sha256_16") != source_digest(FFN_SOURCE)):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -125,9 +130,10 @@ def roofline(bytes_, flops, seconds, dtype):
 def cpu_baseline(cfg, inp, L, n_exp):
     """The oracle, as it stands, timed on the host cores: routing and dispatch of all T
     tokens, then, for the first n_exp touched experts (all of them by default), the FFN
-    of every row routed there and its weighted contribution to the output.  Expert
-    weights are converted to float64 outside the timed region.  Tokens-equivalent =
-    rows computed / k."""
+    of every row routed there and its weighted contribution to the output.  Each expert's
+    weights are regenerated from their seed on the GPU (the bits the layer was given, in
+    the nn.Linear layout) and converted to float64 outside the timed region.
+    Tokens-equivalent = rows computed / k."""
     from oracle import moe_oracle as O
     from sparse_mixture_experts_27_amd import synth
     try:
@@ -149,9 +155,7 @@ def cpu_baseline(cfg, inp, L, n_exp):
     experts = [int(e) for e in np.nonzero(kept)[0][:n_exp]]
     rows = 0
     for e in experts:
-        wts = (synth.to_numpy(inp["w_gate"][e]),
-               None if inp["w_up"] is None else synth.to_numpy(inp["w_up"][e]),
-               synth.to_numpy(inp["w_down"][e]))
+        wts = tuple(synth.to_numpy(t) for t in synth.expert_weights(cfg, e, inp["x"].device))
         r = np.arange(dp["offsets"][e], dp["offsets"][e + 1])
         slots = dp["perm"][r]
         tok, j = slots // cfg.k, slots % cfg.k
@@ -193,9 +197,17 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     inp = synth.make_inputs(cfg, dev)
+    packed = args.layout == "packed" and cfg.dtype == "bf16"
+    if packed:
+        # one tensor at a time, each linear copy freed once its packed copy exists
+        for name in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down"):
+            if inp[name] is not None:
+                inp[name] = B.pack_weights(inp[name])
+                torch.cuda.synchronize()
+                torch.cuda.empty_cache()
     L = B.Layer(inp["w_r"], inp["w_gate"], inp["w_up"], inp["w_down"], cfg.k, act=cfg.act, bias=inp["bias"],
                 capacity=cfg.capacity, s_gate=inp["s_gate"], s_up=inp["s_up"], s_down=inp["s_down"],
-                weights=cfg.weights, priority=cfg.priority, overflow=cfg.overflow)
+                weights=cfg.weights, priority=cfg.priority, overflow=cfg.overflow, prepacked=packed)
     x = inp["x"]
     for _ in range(args.warmup):
         L(x)
@@ -223,7 +235,7 @@ def main():
     alg = algorithmic(cfg, touched, rows)
     up_s = stage_ms["ffn_up"] / 1e3
     roof = roofline(alg["up_bytes"], alg["up_flops"], up_s, cfg.dtype)
-    roof["traffic"] = measured_traffic(cfg.name)
+    roof["traffic"] = measured_traffic(cfg.name, "packed" if packed else "linear")
     roof["kernel"] = "ffn_gemm_bf16_kernel<SwiGLU up>" if cfg.dtype == "bf16" else "ffn_gemm_f32_kernel<up>"
     layer_roof = roofline(alg["layer_bytes"], alg["layer_flops"], ms_step / 1e3, cfg.dtype)
     # the metric also asks for the share of the MFMA peak, whichever roof binds
@@ -248,7 +260,8 @@ def main():
         "data": "synthetic (seeded N(0,1) hidden states, N(0,1/fan_in) random-init weights)",
         "config": {"workload": cfg.label, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k, "F": cfg.F,
                    "act": cfg.act, "shared": cfg.shared, "capacity": cfg.capacity, "priority": cfg.priority,
-                   "overflow": cfg.overflow, "parallelism": "single-gpu"},
+                   "overflow": cfg.overflow, "weight_layout": "packed" if packed else "linear",
+                   "parallelism": "single-gpu"},
         "roofline": roof,
         "mfma_utilization": mfma,
         "layer_roofline": layer_roof,

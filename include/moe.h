@@ -79,6 +79,13 @@ typedef enum { MOE_PRIORITY_TOKEN = 0, MOE_PRIORITY_SLOT = 1 } moe_priority_t;
  *                         earlier re-routes that still has room, else are dropped; a moved
  *                         slot keeps its routing weight */
 typedef enum { MOE_OVERFLOW_DROP = 0, MOE_OVERFLOW_REROUTE = 1 } moe_overflow_t;
+/* Storage order of the bf16 expert weights (w_gate, w_up, w_down and the shared expert's):
+ *   MOE_LAYOUT_LINEAR  the nn.Linear layout [G, N, K], K contiguous
+ *   MOE_LAYOUT_PACKED  the same values reordered by moe_pack_weights into MFMA operand
+ *                      fragments (same size); the expert FFN then reads each 16 x 32
+ *                      fragment as one contiguous KiB.  The results are bit-identical to
+ *                      the linear layout's. */
+typedef enum { MOE_LAYOUT_LINEAR = 0, MOE_LAYOUT_PACKED = 1 } moe_layout_t;
 
 /* Static description of a status code (host). */
 const char* moe_status_string(moe_status_t s);
@@ -139,6 +146,21 @@ moe_status_t moe_dispatch(const int32_t* topk_idx, const float* logits, int64_t 
                           int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
                           int32_t* n_dropped, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * moe_pack_weights - reorder stacked bf16 expert weights for the expert FFN.
+ *   [cnnet]: the experts' weights are stacked in one tensor and sliced by expert index;
+ *   this is a one-time change of that tensor's storage order, done when the weights are
+ *   loaded, not part of a forward pass.
+ *   w       [G, N, K] bf16 in, nn.Linear layout (w_gate / w_up: N = F, K = d;
+ *           w_down: N = d, K = F; a shared expert's weights with G = 1)
+ *   packed  [G, N, K] bf16 out (same size, must not overlap w): 16-byte chunk
+ *           c = ((g * N/16 + i) * K/32 + j) * 64 + l holds w[g][16 i + l % 16][32 j + 8 (l / 16) + 0..7]
+ *   Requirements: G >= 1, N % 16 == 0 and K % 32 == 0 (MOE_EUNSUPPORTED otherwise).
+ * Pure data movement, deterministic.
+ */
+moe_status_t moe_pack_weights(const void* w, void* packed, int64_t G, int64_t N, int64_t K,
+                              hipStream_t stream);
+
 /* Workspace bytes moe_expert_ffn needs (host, pure). */
 size_t moe_expert_ffn_workspace_bytes(int64_t max_rows, int32_t G, int64_t d, int64_t F,
                                       moe_act_t act, moe_dtype_t dt);
@@ -154,13 +176,14 @@ size_t moe_expert_ffn_workspace_bytes(int64_t max_rows, int32_t G, int64_t d, in
  *   offsets  [G+1] int32 (device): group g owns rows [offsets[g], offsets[g+1]),
  *            non-decreasing, offsets[0] >= 0.  Rows at or beyond max_rows are ignored.
  *   max_rows host upper bound of offsets[G] (sizes the launch and the workspace)
+ *   layout   moe_layout_t of w_gate, w_up and w_down (MOE_LAYOUT_PACKED: bf16 only)
  *   y        [max_rows, d] fp32 out: y[r] for r < min(offsets[G], max_rows)
  *   ws       device workspace of moe_expert_ffn_workspace_bytes(...) bytes
  */
 moe_status_t moe_expert_ffn(const void* x, const int32_t* perm, int32_t k,
                             const int32_t* offsets, int32_t G, int64_t max_rows,
                             int64_t d, int64_t F, moe_act_t act, moe_dtype_t dt,
-                            const void* w_gate, const void* w_up, const void* w_down,
+                            moe_layout_t layout, const void* w_gate, const void* w_up, const void* w_down,
                             float* y, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
@@ -212,6 +235,8 @@ typedef struct moe_layer_args {
   int32_t weights;       /* moe_weights_t (0: renormalised) */
   int32_t priority;      /* moe_priority_t (0: token order) */
   int32_t overflow;      /* moe_overflow_t (0: drop) */
+  int32_t layout;        /* moe_layout_t of the expert weights, routed and shared (0: linear;
+                            packed needs dt = MOE_BF16) */
   int64_t T, d, F;
   int32_t E, k;
   int64_t capacity;      /* <= 0: unlimited */

@@ -22,12 +22,13 @@ MOE_ACT_GELU, MOE_ACT_SWIGLU = 0, 1
 WEIGHT_MODES = {"renormalized": 0, "softmax": 1}
 PRIORITIES = {"token": 0, "slot": 1}
 OVERFLOWS = {"drop": 0, "reroute": 1}
+MOE_LAYOUT_LINEAR, MOE_LAYOUT_PACKED = 0, 1
 STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EUNSUPPORTED", 3: "MOE_EWORKSPACE", 4: "MOE_EHIP"}
 
 # entry points declared in include/moe.h
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_route_workspace_bytes", "moe_route",
            "moe_dispatch_workspace_bytes",
-           "moe_dispatch", "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine",
+           "moe_dispatch", "moe_pack_weights", "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine",
            "moe_routing_stats_workspace_bytes", "moe_routing_stats",
            "moe_layer_workspace_bytes", "moe_layer_forward")
 
@@ -40,7 +41,7 @@ class MoEError(RuntimeError):
 
 class LayerArgs(C.Structure):
     _fields_ = [("dt", C.c_int32), ("act", C.c_int32), ("out_dt", C.c_int32), ("weights", C.c_int32),
-                ("priority", C.c_int32), ("overflow", C.c_int32),
+                ("priority", C.c_int32), ("overflow", C.c_int32), ("layout", C.c_int32),
                 ("T", C.c_int64), ("d", C.c_int64), ("F", C.c_int64),
                 ("E", C.c_int32), ("k", C.c_int32), ("capacity", C.c_int64),
                 ("x", C.c_void_p), ("w_r", C.c_void_p), ("bias", C.c_void_p),
@@ -86,10 +87,12 @@ def lib():
         L.moe_dispatch_workspace_bytes.argtypes = [i64, i32, i32]
         L.moe_dispatch.restype = C.c_int
         L.moe_dispatch.argtypes = [vp, vp, i64, i32, i32, i64, C.c_int, C.c_int, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_pack_weights.restype = C.c_int
+        L.moe_pack_weights.argtypes = [vp, vp, i64, i64, i64, vp]
         L.moe_expert_ffn_workspace_bytes.restype = sz
         L.moe_expert_ffn_workspace_bytes.argtypes = [i64, i32, i64, i64, C.c_int, C.c_int]
         L.moe_expert_ffn.restype = C.c_int
-        L.moe_expert_ffn.argtypes = [vp, vp, i32, vp, i32, i64, i64, i64, C.c_int, C.c_int,
+        L.moe_expert_ffn.argtypes = [vp, vp, i32, vp, i32, i64, i64, i64, C.c_int, C.c_int, C.c_int,
                                      vp, vp, vp, vp, vp, sz, vp]
         L.moe_combine.restype = C.c_int
         L.moe_combine.argtypes = [vp, i64, vp, vp, vp, i64, i64, i32, C.c_int, vp, vp]
@@ -188,8 +191,22 @@ def dispatch(topk_idx, E, capacity=0, priority="token", overflow="drop", logits=
     return Dispatch(counts, offsets, perm, inv, nd)
 
 
-def expert_ffn(x, offsets, w_gate, w_up, w_down, max_rows, perm=None, k=1, act="swiglu"):
-    """-> y f32 [max_rows, d] (rows past offsets[G] unspecified)."""
+def pack_weights(w):
+    """bf16 expert weights [G, N, K] (or [N, K]) in the nn.Linear layout -> a new tensor of
+    the same shape holding them in the packed layout (moe_pack_weights)."""
+    _req(w, "w", torch.bfloat16)
+    shape = w.shape
+    w3 = w if w.dim() == 3 else w.unsqueeze(0)
+    G, N, K = w3.shape
+    out = torch.empty_like(w)
+    _check(lib().moe_pack_weights(_ptr(w3), _ptr(out), G, N, K, _stream(w.device)))
+    assert out.shape == shape
+    return out
+
+
+def expert_ffn(x, offsets, w_gate, w_up, w_down, max_rows, perm=None, k=1, act="swiglu", packed=False):
+    """-> y f32 [max_rows, d] (rows past offsets[G] unspecified).  packed: the weights were
+    reordered by pack_weights."""
     G = w_gate.shape[0]
     F, d = w_gate.shape[1], w_gate.shape[2]
     dev = x.device
@@ -201,7 +218,7 @@ def expert_ffn(x, offsets, w_gate, w_up, w_down, max_rows, perm=None, k=1, act="
     y = torch.empty((max(max_rows, 1), d), dtype=torch.float32, device=dev)
     ws = _ws(lib().moe_expert_ffn_workspace_bytes(max_rows, G, d, F, a, _dt(x)), dev)
     _check(lib().moe_expert_ffn(_ptr(x), _ptr(perm), k, _ptr(offsets), G, max_rows, d, F, a, _dt(x),
-                                _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(y), _ptr(ws), ws.numel(),
+                                MOE_LAYOUT_PACKED if packed else MOE_LAYOUT_LINEAR, _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(y), _ptr(ws), ws.numel(),
                                 _stream(dev)))
     return y[:max_rows]
 
@@ -240,13 +257,16 @@ class Layer:
     """One MoE layer with its weights; forward() runs moe_layer_forward.
 
     Buffers for the output, the routing results and the workspace are allocated once
-    (per token count) and reused, so repeated calls allocate nothing.
+    (per token count) and reused, so repeated calls allocate nothing.  packed=True
+    stores bf16 expert weights (routed and shared) in the packed layout: they are
+    reordered once here, into new tensors (the caller's tensors are left as they are).
+    prepacked=True: the expert weights given are already packed (pack_weights).
     """
 
     def __init__(self, w_r, w_gate, w_up, w_down, k, act="swiglu", bias=None, capacity=0,
                  s_gate=None, s_up=None, s_down=None, out_dtype=torch.float32, stats=False,
                  lambda_balance=0.01, lambda_aux=0.01, gamma_aux=100.0, weights="renormalized",
-                 priority="token", overflow="drop"):
+                 priority="token", overflow="drop", packed=False, prepacked=False):
         self.w_r, self.bias = w_r, bias
         self.w_gate, self.w_up, self.w_down = w_gate, w_up, w_down
         self.s_gate, self.s_up, self.s_down = s_gate, s_up, s_down
@@ -267,6 +287,11 @@ class Layer:
                      (s_gate, "s_gate"), (s_up, "s_up"), (s_down, "s_down")):
             _req(t, n, w_r.dtype, dev)
         _req(bias, "bias", torch.float32, dev)
+        self.layout = MOE_LAYOUT_PACKED if packed or prepacked else MOE_LAYOUT_LINEAR
+        if packed and not prepacked:
+            self.w_gate, self.w_up, self.w_down, self.s_gate, self.s_up, self.s_down = (
+                None if t is None else pack_weights(t)
+                for t in (w_gate, w_up, w_down, s_gate, s_up, s_down))
         self._T = None
 
     def _args(self, x):
@@ -277,6 +302,7 @@ class Layer:
         a.weights = self.weight_mode
         a.priority = self.priority
         a.overflow = self.overflow
+        a.layout = self.layout
         a.T, a.d, a.F, a.E, a.k, a.capacity = T, self.d, self.F, self.E, self.k, self.capacity
         a.x, a.w_r, a.bias = _ptr(x), _ptr(self.w_r), _ptr(self.bias)
         a.w_gate, a.w_up, a.w_down = _ptr(self.w_gate), _ptr(self.w_up), _ptr(self.w_down)

@@ -54,6 +54,14 @@ namespace {
 bool valid_dt(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
 bool valid_act(int a) { return a == MOE_ACT_GELU || a == MOE_ACT_SWIGLU; }
 
+moe_status_t check_layout(int layout, int dt) {
+  if (layout != MOE_LAYOUT_LINEAR && layout != MOE_LAYOUT_PACKED)
+    return fail(MOE_EINVAL, "weight layout %d is not MOE_LAYOUT_LINEAR or MOE_LAYOUT_PACKED", layout);
+  if (layout == MOE_LAYOUT_PACKED && dt != MOE_BF16)
+    return fail(MOE_EINVAL, "the packed weight layout is defined for bf16 weights only");
+  return MOE_OK;
+}
+
 moe_status_t check_route_args(const void* x, const void* w_r, int dt, int64_t T, int64_t d, int E, int k,
                               const void* topk_idx, const void* topk_w, const void* logits) {
   if (!valid_dt(dt)) return fail(MOE_EINVAL, "dtype %d is not MOE_F32 or MOE_BF16", dt);
@@ -174,19 +182,36 @@ size_t moe_expert_ffn_workspace_bytes(int64_t max_rows, int32_t G, int64_t d, in
   return ffn_plan(max_rows, G, 0, d, F, act, dt).ws_bytes;
 }
 
+moe_status_t moe_pack_weights(const void* w, void* packed, int64_t G, int64_t N, int64_t K, hipStream_t stream) {
+  g_last_error[0] = 0;
+  if (G < 1 || N < 1 || K < 1) return fail(MOE_EINVAL, "G, N and K must be >= 1");
+  if (N % 16 != 0 || K % 32 != 0)
+    return fail(MOE_EUNSUPPORTED, "packing needs N %% 16 == 0 and K %% 32 == 0 (N=%lld K=%lld)", (long long)N,
+                (long long)K);
+  if (N > (int64_t{1} << 40) / K || G > (int64_t{1} << 60) / (N * K))
+    return fail(MOE_EINVAL, "G*N*K too large");
+  if (!w || !packed) return fail(MOE_EINVAL, "moe_pack_weights: null pointer");
+  if (!aligned16(w) || !aligned16(packed)) return fail(MOE_EINVAL, "w and packed must be 16-byte aligned");
+  const uintptr_t bytes = static_cast<uintptr_t>(G * N * K) * 2;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(w), b = reinterpret_cast<uintptr_t>(packed);
+  if (a < b + bytes && b < a + bytes) return fail(MOE_EINVAL, "w and packed overlap");
+  return launch_pack(w, packed, G, N, K, stream);
+}
+
 moe_status_t moe_expert_ffn(const void* x, const int32_t* perm, int32_t k, const int32_t* offsets, int32_t G,
                             int64_t max_rows, int64_t d, int64_t F, moe_act_t act, moe_dtype_t dt,
-                            const void* w_gate, const void* w_up, const void* w_down, float* y, void* ws,
-                            size_t ws_bytes, hipStream_t stream) {
+                            moe_layout_t layout, const void* w_gate, const void* w_up, const void* w_down, float* y,
+                            void* ws, size_t ws_bytes, hipStream_t stream) {
   g_last_error[0] = 0;
   if (moe_status_t st = check_ffn_args(x, offsets, G, max_rows, d, F, act, dt, w_gate, w_up, w_down, y)) return st;
+  if (moe_status_t st = check_layout(layout, dt)) return st;
   if (perm && k < 1) return fail(MOE_EINVAL, "k must be >= 1 when perm is given");
   const FfnPlan plan = ffn_plan(max_rows, G, 0, d, F, act, dt);
   if (!ws || ws_bytes < plan.ws_bytes)
     return fail(MOE_EWORKSPACE, "expert FFN needs %zu workspace bytes, got %zu", plan.ws_bytes, ws_bytes);
   FfnProblem p{};
   p.x = x; p.perm = perm; p.k = k; p.offsets = offsets; p.G = G; p.max_rows = max_rows;
-  p.d = d; p.F = F; p.act = act; p.dt = dt;
+  p.d = d; p.F = F; p.act = act; p.dt = dt; p.layout = layout;
   p.w_gate = w_gate; p.w_up = act == MOE_ACT_SWIGLU ? w_up : nullptr; p.w_down = w_down;
   return launch_ffn(p, plan, y, /*reduce_splits=*/true, ws, stream);
 }
@@ -278,6 +303,7 @@ moe_status_t moe_layer_forward(const moe_layer_args_t* a, hipStream_t stream) {
     return fail(MOE_EINVAL, "overflow %d invalid", a->overflow);
   if (a->overflow == MOE_OVERFLOW_REROUTE && a->T * a->k > (int64_t{1} << 29))
     return fail(MOE_EUNSUPPORTED, "re-routing supports at most 2^29 slots");
+  if (moe_status_t st = check_layout(a->layout, a->dt)) return st;
   if (a->F < 1) return fail(MOE_EINVAL, "F must be >= 1");
   if (a->dt == MOE_BF16 && (a->d % 64 != 0 || a->F % 64 != 0))
     return fail(MOE_EUNSUPPORTED, "bf16 layer needs d and F multiples of 64");
@@ -332,7 +358,7 @@ moe_status_t moe_layer_forward(const moe_layer_args_t* a, hipStream_t stream) {
   mark(2);
   FfnProblem p{};
   p.x = a->x; p.perm = perm; p.k = a->k; p.offsets = offsets; p.G = a->E; p.max_rows = max_rows;
-  p.d = a->d; p.F = a->F; p.act = a->act; p.dt = a->dt;
+  p.d = a->d; p.F = a->F; p.act = a->act; p.dt = a->dt; p.layout = a->layout;
   p.w_gate = a->w_gate; p.w_up = swiglu ? a->w_up : nullptr; p.w_down = a->w_down;
   p.s_gate = a->s_gate; p.s_up = swiglu ? a->s_up : nullptr; p.s_down = a->s_down;
   p.shared_rows = shared ? T : 0;

@@ -66,6 +66,7 @@ struct FfnProblem {
   int64_t max_rows;         // rows of y / H allocated
   int64_t d, F;
   int act, dt;
+  int layout;               // moe_layout_t of every expert weight below
   const void* w_gate; const void* w_up; const void* w_down;       // [G, ...]
   const void* s_gate; const void* s_up; const void* s_down;       // shared or null
   int64_t shared_rows;      // 0 = no shared group
@@ -88,6 +89,9 @@ FfnPlan ffn_plan(int64_t max_rows, int G, int64_t shared_rows, int64_t d, int64_
 // ev (nullable): events recorded after the schedule, up-projection and down-projection.
 moe_status_t launch_ffn(const FfnProblem& p, const FfnPlan& plan, float* y, bool reduce_splits,
                         void* ws, hipStream_t s, void* const* ev = nullptr);
+
+// Fragment packing of bf16 weights [G, N, K] (moe_pack_weights; sizes already checked).
+moe_status_t launch_pack(const void* w, void* packed, int64_t G, int64_t N, int64_t K, hipStream_t s);
 
 size_t stats_ws_bytes(int64_t T);
 moe_status_t launch_stats(const float* logits, const int32_t* counts, const int32_t* n_dropped, int64_t T, int E,

@@ -205,7 +205,7 @@ __device__ __forceinline__ int64_t a_source_row(const GemmArgs& p, int mode, int
 // uniform base, 32-bit per-lane offset, uniform stage offset.  The LDS slots arrive as
 // distinct restrict pointers so the compiler can tell a slot being read from the slots
 // being filled and does not wait for those loads before its LDS reads.
-template <int MODE, int MT, int NW>
+template <int MODE, int MT, int NW, bool PK>
 __device__ __forceinline__ void ffn_gemm_bf16_body(const GemmArgs& p, uint16_t* __restrict__ L0,
                                                    uint16_t* __restrict__ L1, uint16_t* __restrict__ L2) {
   constexpr int NT = NW * 64;                     // threads
@@ -240,6 +240,18 @@ __device__ __forceinline__ void ffn_gemm_bf16_body(const GemmArgs& p, uint16_t* 
   const char* Wb0 = reinterpret_cast<const char*>(static_cast<const uint16_t*>(shared_grp ? p.sw0 : p.w0) + wstride);
   const char* Wb1 = reinterpret_cast<const char*>(static_cast<const uint16_t*>(shared_grp ? p.sw1 : p.w1) + wstride);
   if (MODE != MODE_SWIGLU_UP) Wb1 = Wb0;
+  // Weight byte offsets.  Linear layout [N_w, K]: lane (row, kgroup) reads 8 elements at
+  // K = 8*kgroup of its row; the two k32 steps of a stage are 64 B apart, stages 128 B,
+  // and one load covers 64 contiguous bytes of each of 16 rows.  Packed layout
+  // [N_w/16][K/32][64 lanes][8]: each 16-row x 32-K fragment is one contiguous KiB in
+  // lane order, so one load reads 1 KiB contiguous; k32 steps 1 KiB apart, stages 2 KiB.
+  constexpr int W_STEP = PK ? 1024 : 64;
+  constexpr int W_STAGE = PK ? 2048 : BK * 2;
+  auto woff = [&](int64_t row) -> uint32_t {
+    const int kg = lane >> 4;
+    if (PK) return static_cast<uint32_t>((((row >> 4) * (p.K >> 5) + (k_begin >> 5)) * 64 + (row & 15) + 16 * kg) * 16);
+    return static_cast<uint32_t>((row * p.K + k_begin + 8 * kg) * 2);
+  };
   int64_t col_base;                         // first output column of this wave
   if (MODE == MODE_SWIGLU_UP) col_base = static_cast<int64_t>(ti.ntile) * 128 + wave * (WCOLS / 2);   // hidden unit
   else col_base = static_cast<int64_t>(ti.ntile) * 256 + wave * WCOLS;
@@ -251,7 +263,7 @@ __device__ __forceinline__ void ffn_gemm_bf16_body(const GemmArgs& p, uint16_t* 
                  : (MODE == MODE_SWIGLU_UP) ? col_base + (nf % (NF / 2)) * 16 + (lane & 15)
                                             : col_base + nf * 16 + (lane & 15);
     if (!wave_on) wrow = lane & 15;         // a valid row; the result is not stored
-    boff[nf] = static_cast<uint32_t>((wrow * p.K + k_begin + 8 * (lane >> 4)) * 2);
+    boff[nf] = woff(wrow);
   }
   // paired layout: this lane's weight row lives in the gate or the up tensor
   const char* wlane = PAIRED ? ((lane & 8) ? Wb1 : Wb0) + boff[0] : nullptr;
@@ -320,10 +332,10 @@ __device__ __forceinline__ void ffn_gemm_bf16_body(const GemmArgs& p, uint16_t* 
   };
   auto load_b = [&](int st, int slot) {
     st = clamp_stage(st);
-    const int ko = st * (BK * 2);           // uniform part of the offset
+    const int ko = st * W_STAGE;            // uniform part of the offset
     if (PAIRED) {                           // per-lane tensor: a 64-bit address
 #pragma unroll
-      for (int s = 0; s < 2; ++s) rb[slot][s][0] = *reinterpret_cast<const bf16x8*>(wlane + ko + s * 64);
+      for (int s = 0; s < 2; ++s) rb[slot][s][0] = *reinterpret_cast<const bf16x8*>(wlane + ko + s * W_STEP);
       return;
     }
 #pragma unroll
@@ -331,7 +343,7 @@ __device__ __forceinline__ void ffn_gemm_bf16_body(const GemmArgs& p, uint16_t* 
 #pragma unroll
       for (int nf = 0; nf < NF; ++nf) {
         const auto& rs = (MODE == MODE_SWIGLU_UP && nf >= NF / 2) ? w1rsrc : w0rsrc;
-        rb[slot][s][nf] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, boff[nf] + s * 64, ko, 0));
+        rb[slot][s][nf] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, boff[nf] + s * W_STEP, ko, 0));
       }
   };
   // Mark a weight slot as consumed on every path (the MFMAs that read it sit behind the
@@ -486,12 +498,30 @@ pipeline_done:
   }
 }
 
-template <int MODE, int MT, int NW>
+template <int MODE, int MT, int NW, bool PK>
 __global__ __launch_bounds__(NW * 64, 1) void ffn_gemm_bf16_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint16_t As0[MT * 16 * BK];
   __shared__ __attribute__((aligned(16))) uint16_t As1[MT * 16 * BK];
   __shared__ __attribute__((aligned(16))) uint16_t As2[MT * 16 * BK];
-  ffn_gemm_bf16_body<MODE, MT, NW>(p, As0, As1, As2);
+  ffn_gemm_bf16_body<MODE, MT, NW, PK>(p, As0, As1, As2);
+}
+
+// Fragment packing of bf16 weights [G, N, K] (K contiguous): 16-byte chunk c of the
+// output, with c = ((g * N/16 + i) * K/32 + j) * 64 + l, holds the 8 elements of row
+// 16 i + l % 16 at K = 32 j + 8 (l / 16): the 64 lanes of one 16 x 32 MFMA operand
+// fragment in lane order.
+__global__ __launch_bounds__(256) void pack_weights_kernel(const u32x4* __restrict__ w, u32x4* __restrict__ out,
+                                                           int64_t N, int64_t K, int64_t total) {
+  const int64_t kb = K >> 5, nb = N >> 4;
+  for (int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; c < total;
+       c += static_cast<int64_t>(gridDim.x) * 256) {
+    const int l = static_cast<int>(c & 63);
+    const int64_t blk = c >> 6;
+    const int64_t j = blk % kb;
+    const int64_t gi = blk / kb;              // g * N/16 + i
+    const int64_t row = (gi / nb) * N + (gi % nb) * 16 + (l & 15);
+    out[c] = w[(row * K + j * 32 + (l >> 4) * 8) >> 3];
+  }
 }
 
 // ---- fp32 path: 64 x 64 output tile, 256 threads x (4 x 4), K staged 16 at a time.
@@ -582,31 +612,37 @@ __global__ __launch_bounds__(256) void ffn_reduce_splits_kernel(const float* __r
 }
 
 // Launch one bf16 grouped GEMM with the M-tile (MT*16 rows) chosen by the plan.
-template <int MODE>
-void launch_bf16_gemm(int bm, int nw, int64_t grid, const GemmArgs& g, hipStream_t s) {
+template <int MODE, bool PK>
+void launch_bf16_gemm_l(int bm, int nw, int64_t grid, const GemmArgs& g, hipStream_t s) {
   const unsigned gr = static_cast<unsigned>(grid);
   if (nw == 16) {
     switch (bm) {
-      case 32: ffn_gemm_bf16_kernel<MODE, 2, 16><<<gr, 1024, 0, s>>>(g); break;
-      case 64: ffn_gemm_bf16_kernel<MODE, 4, 16><<<gr, 1024, 0, s>>>(g); break;
-      case 128: ffn_gemm_bf16_kernel<MODE, 8, 16><<<gr, 1024, 0, s>>>(g); break;
-      default: ffn_gemm_bf16_kernel<MODE, 16, 16><<<gr, 1024, 0, s>>>(g); break;
+      case 32: ffn_gemm_bf16_kernel<MODE, 2, 16, PK><<<gr, 1024, 0, s>>>(g); break;
+      case 64: ffn_gemm_bf16_kernel<MODE, 4, 16, PK><<<gr, 1024, 0, s>>>(g); break;
+      case 128: ffn_gemm_bf16_kernel<MODE, 8, 16, PK><<<gr, 1024, 0, s>>>(g); break;
+      default: ffn_gemm_bf16_kernel<MODE, 16, 16, PK><<<gr, 1024, 0, s>>>(g); break;
     }
   } else if (nw == 8) {
     switch (bm) {
-      case 32: ffn_gemm_bf16_kernel<MODE, 2, 8><<<gr, 512, 0, s>>>(g); break;
-      case 64: ffn_gemm_bf16_kernel<MODE, 4, 8><<<gr, 512, 0, s>>>(g); break;
-      case 128: ffn_gemm_bf16_kernel<MODE, 8, 8><<<gr, 512, 0, s>>>(g); break;
-      default: ffn_gemm_bf16_kernel<MODE, 16, 8><<<gr, 512, 0, s>>>(g); break;
+      case 32: ffn_gemm_bf16_kernel<MODE, 2, 8, PK><<<gr, 512, 0, s>>>(g); break;
+      case 64: ffn_gemm_bf16_kernel<MODE, 4, 8, PK><<<gr, 512, 0, s>>>(g); break;
+      case 128: ffn_gemm_bf16_kernel<MODE, 8, 8, PK><<<gr, 512, 0, s>>>(g); break;
+      default: ffn_gemm_bf16_kernel<MODE, 16, 8, PK><<<gr, 512, 0, s>>>(g); break;
     }
   } else {
     switch (bm) {
-      case 32: ffn_gemm_bf16_kernel<MODE, 2, 4><<<gr, 256, 0, s>>>(g); break;
-      case 64: ffn_gemm_bf16_kernel<MODE, 4, 4><<<gr, 256, 0, s>>>(g); break;
-      case 128: ffn_gemm_bf16_kernel<MODE, 8, 4><<<gr, 256, 0, s>>>(g); break;
-      default: ffn_gemm_bf16_kernel<MODE, 16, 4><<<gr, 256, 0, s>>>(g); break;
+      case 32: ffn_gemm_bf16_kernel<MODE, 2, 4, PK><<<gr, 256, 0, s>>>(g); break;
+      case 64: ffn_gemm_bf16_kernel<MODE, 4, 4, PK><<<gr, 256, 0, s>>>(g); break;
+      case 128: ffn_gemm_bf16_kernel<MODE, 8, 4, PK><<<gr, 256, 0, s>>>(g); break;
+      default: ffn_gemm_bf16_kernel<MODE, 16, 4, PK><<<gr, 256, 0, s>>>(g); break;
     }
   }
+}
+
+template <int MODE>
+void launch_bf16_gemm(bool packed, int bm, int nw, int64_t grid, const GemmArgs& g, hipStream_t s) {
+  if (packed) launch_bf16_gemm_l<MODE, true>(bm, nw, grid, g, s);
+  else launch_bf16_gemm_l<MODE, false>(bm, nw, grid, g, s);
 }
 
 }  // namespace
@@ -665,6 +701,7 @@ moe_status_t launch_ffn(const FfnProblem& p, const FfnPlan& plan, float* y, bool
   const bool has_shared = p.shared_rows > 0;
   const int Gt = p.G + (has_shared ? 1 : 0);
   const bool bf = p.dt == MOE_BF16;
+  const bool packed = p.layout == MOE_LAYOUT_PACKED;
   const int bm = plan.bm;
   WsCarver c(ws);
   int32_t* sched = c.take<int32_t>(sched_words(Gt));
@@ -705,8 +742,8 @@ moe_status_t launch_ffn(const FfnProblem& p, const FfnPlan& plan, float* y, bool
   if (bf) {
     g.nt = static_cast<int>(swiglu ? (p.F + 127) / 128 : (p.F + 255) / 256);
     const int64_t grid = ((plan.max_mtiles * g.nt + 7) / 8) * 8;
-    if (swiglu) launch_bf16_gemm<MODE_SWIGLU_UP>(bm, plan.nw, grid, g, s);
-    else launch_bf16_gemm<MODE_GELU_UP>(bm, plan.nw, grid, g, s);
+    if (swiglu) launch_bf16_gemm<MODE_SWIGLU_UP>(packed, bm, plan.nw, grid, g, s);
+    else launch_bf16_gemm<MODE_GELU_UP>(packed, bm, plan.nw, grid, g, s);
   } else {
     g.nt = static_cast<int>((p.F + 63) / 64);
     const int64_t grid = ((plan.max_mtiles * g.nt + 7) / 8) * 8;
@@ -732,7 +769,7 @@ moe_status_t launch_ffn(const FfnProblem& p, const FfnPlan& plan, float* y, bool
     g.split_stride = p.max_rows * p.d;
     g.out = plan.splits > 1 && reduce_splits ? static_cast<void*>(part) : static_cast<void*>(y);
     const int64_t grid = ((plan.max_mtiles * g.nt * g.splits + 7) / 8) * 8;
-    launch_bf16_gemm<MODE_DOWN>(bm, plan.nw, grid, g, s);
+    launch_bf16_gemm<MODE_DOWN>(packed, bm, plan.nw, grid, g, s);
   } else {
     g.nt = static_cast<int>((p.d + 63) / 64);
     g.k_chunk = p.F;
@@ -749,6 +786,14 @@ moe_status_t launch_ffn(const FfnProblem& p, const FfnPlan& plan, float* y, bool
     if (moe_status_t st = check_launch("ffn split reduction kernel")) return st;
   }
   return MOE_OK;
+}
+
+moe_status_t launch_pack(const void* w, void* packed, int64_t G, int64_t N, int64_t K, hipStream_t s) {
+  const int64_t total = G * N * K / 8;
+  const int64_t want = (total + 255) / 256;
+  const unsigned grid = static_cast<unsigned>(want < 8192 ? want : 8192);
+  pack_weights_kernel<<<grid, 256, 0, s>>>(static_cast<const u32x4*>(w), static_cast<u32x4*>(packed), N, K, total);
+  return check_launch("weight packing kernel");
 }
 
 }  // namespace moe

@@ -37,11 +37,11 @@ def say(msg: str):
     sys.stdout.flush()
 
 
-def layer_for(cfg, inp, out_dtype=torch.float32):
+def layer_for(cfg, inp, out_dtype=torch.float32, packed=False):
     return B.Layer(inp["w_r"], inp["w_gate"], inp["w_up"], inp["w_down"], cfg.k, act=cfg.act,
                    bias=inp["bias"], capacity=cfg.capacity, s_gate=inp["s_gate"], s_up=inp["s_up"],
                    s_down=inp["s_down"], out_dtype=out_dtype, weights=cfg.weights, priority=cfg.priority,
-                   overflow=cfg.overflow)
+                   overflow=cfg.overflow, packed=packed)
 
 
 def half_ulp_bf16(v: np.ndarray) -> np.ndarray:
@@ -50,8 +50,8 @@ def half_ulp_bf16(v: np.ndarray) -> np.ndarray:
     return np.where(v == 0, 0.0, np.ldexp(1.0, ex - 9))
 
 
-def run_layer(cfg, inp, out_dtype=torch.float32) -> Dict[str, np.ndarray]:
-    L = layer_for(cfg, inp, out_dtype)
+def run_layer(cfg, inp, out_dtype=torch.float32, packed=False) -> Dict[str, np.ndarray]:
+    L = layer_for(cfg, inp, out_dtype, packed)
     out = L(inp["x"])
     torch.cuda.synchronize()
     res = dict(out=out.float().cpu().numpy().astype(np.float64),

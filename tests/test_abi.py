@@ -106,19 +106,42 @@ def test_dispatch_validation(lib):
 def test_ffn_validation(lib):
     need = lib.moe_expert_ffn_workspace_bytes(8192, 64, 4096, 14336, B.MOE_ACT_SWIGLU, B.MOE_BF16)
     assert need >= 8192 * 14336 * 2                     # holds the bf16 hidden activation
-    base = [16, 16, 2, 16, 64, 8192, 4096, 14336, B.MOE_ACT_SWIGLU, B.MOE_BF16, 16, 16, 16, 16, 16, need, None]
+    base = [16, 16, 2, 16, 64, 8192, 4096, 14336, B.MOE_ACT_SWIGLU, B.MOE_BF16, B.MOE_LAYOUT_LINEAR,
+            16, 16, 16, 16, 16, need, None]
     odd = list(base); odd[6] = 4000                    # d % 64 != 0 for bf16
     assert lib.moe_expert_ffn(*odd) == 2
-    no_up = list(base); no_up[11] = None
+    no_up = list(base); no_up[12] = None
     assert lib.moe_expert_ffn(*no_up) == 1
-    small = list(base); small[15] = need - 1
+    small = list(base); small[16] = need - 1
     assert lib.moe_expert_ffn(*small) == 3
     bad_act = list(base); bad_act[8] = 5
     assert lib.moe_expert_ffn(*bad_act) == 1
+    bad_layout = list(base); bad_layout[10] = 2
+    assert lib.moe_expert_ffn(*bad_layout) == 1
+    assert b"layout" in lib.moe_last_error()
+    f32_packed = list(base); f32_packed[9] = B.MOE_F32; f32_packed[10] = B.MOE_LAYOUT_PACKED
+    f32_packed[16] = lib.moe_expert_ffn_workspace_bytes(8192, 64, 4096, 14336, B.MOE_ACT_SWIGLU, B.MOE_F32)
+    assert lib.moe_expert_ffn(*f32_packed) == 1
+    assert b"bf16" in lib.moe_last_error()
     huge = list(base); huge[5] = 80000               # H = 80000 x 14336 bf16 rows > 2 GiB
-    huge[15] = lib.moe_expert_ffn_workspace_bytes(80000, 64, 4096, 14336, B.MOE_ACT_SWIGLU, B.MOE_BF16)
+    huge[16] = lib.moe_expert_ffn_workspace_bytes(80000, 64, 4096, 14336, B.MOE_ACT_SWIGLU, B.MOE_BF16)
     assert lib.moe_expert_ffn(*huge) == 2
     assert b"2 GiB" in lib.moe_last_error()
+
+
+def test_pack_validation(lib):
+    mib = 1 << 20
+    assert lib.moe_pack_weights(16 * mib, 64 * mib, 0, 16, 32, None) == 1        # G < 1
+    assert lib.moe_pack_weights(16 * mib, 64 * mib, 2, 24, 64, None) == 2        # N % 16
+    assert lib.moe_pack_weights(16 * mib, 64 * mib, 2, 32, 48, None) == 2        # K % 32
+    assert b"K % 32" in lib.moe_last_error()
+    assert lib.moe_pack_weights(None, 64 * mib, 2, 32, 64, None) == 1
+    assert lib.moe_pack_weights(16 * mib + 8, 64 * mib, 2, 32, 64, None) == 1    # misaligned
+    # 2 x 32 x 64 bf16 = 8 KiB: destinations inside or straddling the source overlap
+    assert lib.moe_pack_weights(16 * mib, 16 * mib + 4096, 2, 32, 64, None) == 1
+    assert lib.moe_pack_weights(16 * mib + 4096, 16 * mib, 2, 32, 64, None) == 1
+    assert b"overlap" in lib.moe_last_error()
+    assert lib.moe_pack_weights(16 * mib, 16 * mib, 1, 1 << 30, 1 << 30, None) == 1   # too large
 
 
 def test_combine_validation(lib):
@@ -147,6 +170,11 @@ def test_layer_validation_and_workspace(lib):
     assert lib.moe_layer_forward(C.byref(a), None) == 1
     a.priority, a.overflow = 1, 5
     assert lib.moe_layer_forward(C.byref(a), None) == 1
+    a.layout = 2
+    assert lib.moe_layer_forward(C.byref(a), None) == 1
+    a.layout, a.dt = B.MOE_LAYOUT_PACKED, B.MOE_F32
+    assert lib.moe_layer_forward(C.byref(a), None) == 1
+    a.dt = B.MOE_BF16
     a.overflow = 1
     a.d = 4000
     assert lib.moe_layer_forward(C.byref(a), None) == 2

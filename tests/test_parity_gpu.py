@@ -61,9 +61,9 @@ def _x64(inp):
     return synth.to_numpy(inp["x"]), synth.to_numpy(inp["w_r"]), synth.to_numpy(inp["bias"])
 
 
-def _run_and_check(cfg, inp, tokens=None, out_dtype=torch.float32):
-    say(f"[case] {cfg.label} out={out_dtype}")
-    res = run_layer(cfg, inp, out_dtype)
+def _run_and_check(cfg, inp, tokens=None, out_dtype=torch.float32, packed=False):
+    say(f"[case] {cfg.label} out={out_dtype} packed={packed}")
+    res = run_layer(cfg, inp, out_dtype, packed)
     x64, wr64, b64 = _x64(inp)
     report = {}
     z_o, flip = check_route(cfg, x64, wr64, b64, res, report)
@@ -228,6 +228,72 @@ def test_stage_entry_points():
     assert np.abs(got - ref).max() <= 2e-2 * np.sqrt(np.mean(ref ** 2))
 
 
+def _pack_reference(w: np.ndarray) -> np.ndarray:
+    """The packed layout written out from its definition: chunk ((g*N/16 + i)*K/32 + j)*64 + l
+    holds w[g, 16i + l%16, 32j + 8(l//16) : +8]."""
+    G, N, K = w.shape
+    out = np.empty(G * N * K, dtype=w.dtype)
+    c = 0
+    for g in range(G):
+        for i in range(N // 16):
+            for j in range(K // 32):
+                for lane in range(64):
+                    r, kk = 16 * i + lane % 16, 32 * j + 8 * (lane // 16)
+                    out[c * 8:(c + 1) * 8] = w[g, r, kk:kk + 8]
+                    c += 1
+    return out.reshape(G, N, K)
+
+
+@pytest.mark.parametrize("G,N,K", [(1, 16, 32), (3, 48, 96), (2, 64, 256)])
+def test_pack_weights_layout(G, N, K):
+    gen = torch.Generator().manual_seed(G * 1000 + N + K)
+    bits = torch.randint(-32768, 32768, (G, N, K), generator=gen, dtype=torch.int32).to(torch.int16)
+    w = bits.view(torch.bfloat16).to(DEV)
+    packed = B.pack_weights(w)
+    torch.cuda.synchronize()
+    got = packed.cpu().view(torch.int16).numpy()
+    assert np.array_equal(got, _pack_reference(bits.numpy()))
+    assert torch.equal(w.cpu().view(torch.int16), bits)          # the source is untouched
+    if G == 1:                                                   # a 2-D (shared expert) tensor
+        p2 = B.pack_weights(w[0])
+        torch.cuda.synchronize()
+        assert np.array_equal(p2.cpu().view(torch.int16).numpy(), got[0])
+
+
+# tile height (MOE_TILE_ROWS) and waves per workgroup (MOE_TILE_WAVES); None = the plan's own
+TILES = [None, ("256", "16"), ("128", "4"), ("64", "8"), ("32", "16")]
+
+
+@pytest.mark.parametrize("name", ["bf16-swiglu-multitile", "bf16-gelu", "bf16-shared-bias", "bf16-decode",
+                                  "bf16-capacity-reroute", "bf16-e384-top6-shared"])
+def test_packed_weights_bit_identical(name, monkeypatch):
+    """The packed layout feeds the MFMAs the same operands in the same order: every tile
+    shape gives the same bits as the linear layout under that shape."""
+    cfg = SMALL[name]
+    inp = synth.make_inputs(cfg, DEV)
+    for tile in TILES:
+        if tile is None:
+            monkeypatch.delenv("MOE_TILE_ROWS", raising=False)
+            monkeypatch.delenv("MOE_TILE_WAVES", raising=False)
+        else:
+            monkeypatch.setenv("MOE_TILE_ROWS", tile[0])
+            monkeypatch.setenv("MOE_TILE_WAVES", tile[1])
+        say(f"[case] packed vs linear {cfg.label} tile={tile}")
+        lin = layer_for(cfg, inp)(inp["x"]).clone()
+        pk = layer_for(cfg, inp, packed=True)(inp["x"]).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(lin.view(torch.int32), pk.view(torch.int32)), tile
+
+
+@pytest.mark.parametrize("tile", TILES[1:])
+def test_tile_overrides_against_oracle(tile, monkeypatch):
+    """Every tile shape the tuning overrides can select, packed, against the oracle."""
+    monkeypatch.setenv("MOE_TILE_ROWS", tile[0])
+    monkeypatch.setenv("MOE_TILE_WAVES", tile[1])
+    cfg = SMALL["bf16-shared-bias"]
+    _run_and_check(cfg, synth.make_inputs(cfg, DEV), packed=True)
+
+
 def test_deterministic_bits():
     cfg = SMALL["bf16-shared-bias"]
     inp = synth.make_inputs(cfg, DEV)
@@ -282,6 +348,11 @@ def test_workload_full_size(name):
         rng = np.random.default_rng(cfg.seed)
         tokens = np.sort(rng.choice(np.nonzero(~flip)[0], size=n, replace=False))
     check_output(cfg, x64, z_o, res, expert_fetcher(cfg, inp), shared_weights(inp), tokens, rep)
+    if _expert_weight_bytes(cfg) < 64e9:       # room for a second, packed copy of the weights
+        say(f"[case] full size {cfg.label}: packed weights")
+        out_p = run_layer(cfg, inp, packed=True)["out"]
+        assert np.array_equal(out_p, res["out"])
+        rep["packed"] = "bit-identical"
     rep["n_dropped"] = res["n_dropped"]
     rep["drop_rate"] = res["n_dropped"] / (cfg.T * cfg.k)
     rep["load_min_max"] = (int(res["counts"].min()), int(res["counts"].max()))
@@ -289,6 +360,11 @@ def test_workload_full_size(name):
     say(f"[ok] {cfg.name}: {rep}")
     del inp
     torch.cuda.empty_cache()
+
+
+def _expert_weight_bytes(cfg):
+    mats = 3 if cfg.act == "swiglu" else 2
+    return (cfg.E + (1 if cfg.shared else 0)) * mats * cfg.d * cfg.F * (2 if cfg.dtype == "bf16" else 4)
 
 
 def _check_stats(cfg, stats_gpu, logits, counts, n_dropped, k):
