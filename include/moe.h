@@ -28,7 +28,9 @@
  *     visible after the caller synchronises the stream.  A kernel launch failure
  *     returns MOE_EHIP (work enqueued before it may have run).
  *   - Matrices are row-major and contiguous.  Expert weights use the nn.Linear
- *     layout [out, in]: w_gate / w_up are [G, F, d] and w_down is [G, d, F].
+ *     layout [out, in]: w_gate / w_up are [G, F, d] and w_down is [G, d, F]; bf16
+ *     weights may instead be stored in the packed layout made by moe_pack_weights
+ *     (same shape and size, see moe_layout_t).
  *   - dtype MOE_BF16: x, w_r and expert weights are bfloat16; products are exact in
  *     fp32 and accumulate in fp32; the hidden activation of the expert is rounded to
  *     bf16 once.  MOE_F32: everything is fp32.  Logits, routing weights and the

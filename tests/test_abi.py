@@ -26,9 +26,10 @@ def lib():
     return B.lib()
 
 
-def test_header_declares_the_five_calls():
+def test_header_declares_every_entry_point():
     names = _declared()
-    for n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_layer_forward"):
+    for n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
+              "moe_routing_stats", "moe_pack_weights"):
         assert n in names
     assert set(names) == set(B.EXPORTS)
 
