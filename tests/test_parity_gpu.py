@@ -212,12 +212,22 @@ def test_stage_entry_points():
     yg = y[:R].cpu().numpy().astype(np.float64)
     rms = np.sqrt(np.mean(y_ref ** 2))
     assert np.abs(yg - y_ref).max() <= 2e-2 * rms
+    # the same call on packed weights gives the same bits
+    y_p = B.expert_ffn(inp["x"], dp.offsets, B.pack_weights(inp["w_gate"]), B.pack_weights(inp["w_up"]),
+                       B.pack_weights(inp["w_down"]), cfg.T * cfg.k, perm=dp.perm, k=cfg.k, act=cfg.act,
+                       packed=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y_p[:R].view(torch.int32), y[:R].view(torch.int32))
     # shared expert through the same call: identity rows, one group
     sh_off = torch.tensor([0, cfg.T], dtype=torch.int32, device=DEV)
     ys = B.expert_ffn(inp["x"], sh_off, inp["s_gate"][None], inp["s_up"][None], inp["s_down"][None], cfg.T,
                       act=cfg.act)
     ys_ref = O.expert_ffn(x64, cfg.act, *shared_weights(inp))
     assert np.abs(ys.cpu().numpy() - ys_ref).max() <= 2e-2 * np.sqrt(np.mean(ys_ref ** 2))
+    ys_p = B.expert_ffn(inp["x"], sh_off, B.pack_weights(inp["s_gate"])[None], B.pack_weights(inp["s_up"])[None],
+                        B.pack_weights(inp["s_down"])[None], cfg.T, act=cfg.act, packed=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ys_p.view(torch.int32), ys.view(torch.int32))
     # combine with the shared output
     out = B.combine(y, dp.inv, w, torch.float32, shared=ys)
     torch.cuda.synchronize()
