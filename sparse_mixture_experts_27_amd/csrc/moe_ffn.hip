@@ -695,9 +695,10 @@ FfnPlan ffn_plan(int64_t max_rows, int G, int64_t shared_rows, int64_t d, int64_
     int64_t est = (max_rows + pl.bm - 1) / pl.bm;
     const int64_t busy = G < max_rows ? G : max_rows;
     if (busy > est) est = busy;
-    // split the down projection over K only until there are about 4 tiles per CU: each
-    // split writes fp32 partial sums that the combine reads back
-    while (est * nt2 * pl.splits < 1024 && F / (BK * pl.splits * 2) >= 8) pl.splits *= 2;
+    // split the down projection over K only until there is about one tile per CU: each
+    // split writes fp32 partial sums that the combine reads back (measured with packed
+    // weights: decode T=1..4 fastest at 256 tiles; T=16 and capacity-e16 unsplit)
+    while (est * nt2 * pl.splits < 256 && F / (BK * pl.splits * 2) >= 8) pl.splits *= 2;
   }
   const size_t elem = dt == MOE_BF16 ? 2 : 4;
   size_t ws = align_up(sched_words(Gt) * sizeof(int32_t), 256);
