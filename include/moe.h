@@ -118,6 +118,18 @@ moe_status_t moe_route(const void* x, const void* w_r, const float* bias, moe_dt
                        int32_t* topk_idx, float* topk_w, float* logits, void* ws, size_t ws_bytes,
                        hipStream_t stream);
 
+/*
+ * moe_capacity - per-expert capacity from a capacity factor (host, pure).
+ *   [rkmt] §2.3: each of E experts takes (T*k)/E slots, e.g. (1024*2)/16 = 128; the
+ *   DeepSpeed-MoE block of "MoE混合专家架构原理与工程实践…" §4.2 scales that by a capacity
+ *   factor (1.2 in training, 2.0 at inference) with a floor (min_capacity 4).
+ *   Returns max(min_capacity, ceil(factor * T * k / E)), the product evaluated left to
+ *   right in double precision, clamped to 2^31 - 1.  The result is meant for the
+ *   `capacity` argument of moe_dispatch / moe_layer_args_t, where <= 0 means unlimited.
+ *   Invalid arguments (T < 0, k < 1, E < 1, non-finite factor) return 0 (unlimited).
+ */
+int64_t moe_capacity(int64_t T, int32_t k, int32_t E, double factor, int64_t min_capacity);
+
 /* Workspace bytes moe_dispatch needs for T tokens, E experts, k slots, any policy
  * (host, pure). */
 size_t moe_dispatch_workspace_bytes(int64_t T, int32_t E, int32_t k);

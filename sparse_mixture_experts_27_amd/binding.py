@@ -27,7 +27,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EUNSUPPORTED", 3: "MOE_EWORKSPAC
 
 # entry points declared in include/moe.h
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_route_workspace_bytes", "moe_route",
-           "moe_dispatch_workspace_bytes",
+           "moe_capacity", "moe_dispatch_workspace_bytes",
            "moe_dispatch", "moe_pack_weights", "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine",
            "moe_routing_stats_workspace_bytes", "moe_routing_stats",
            "moe_layer_workspace_bytes", "moe_layer_forward")
@@ -83,6 +83,8 @@ def lib():
         L.moe_route_workspace_bytes.argtypes = [i64, i64, i32, C.c_int]
         L.moe_route.restype = C.c_int
         L.moe_route.argtypes = [vp, vp, vp, C.c_int, i64, i64, i32, i32, C.c_int, vp, vp, vp, vp, sz, vp]
+        L.moe_capacity.restype = i64
+        L.moe_capacity.argtypes = [i64, i32, i32, C.c_double, i64]
         L.moe_dispatch_workspace_bytes.restype = sz
         L.moe_dispatch_workspace_bytes.argtypes = [i64, i32, i32]
         L.moe_dispatch.restype = C.c_int
@@ -161,6 +163,11 @@ def route(x, w_r, k, bias=None, weights="renormalized"):
     _check(lib().moe_route(_ptr(x), _ptr(w_r), _ptr(bias), _dt(x), T, d, E, k, WEIGHT_MODES[weights],
                            _ptr(idx), _ptr(w), _ptr(logits), _ptr(ws), ws.numel(), _stream(x.device)))
     return idx, w, logits
+
+
+def capacity_rule(T, k, E, factor=1.0, min_capacity=0) -> int:
+    """Per-expert capacity max(min_capacity, ceil(factor*T*k/E)) (moe_capacity)."""
+    return int(lib().moe_capacity(int(T), int(k), int(E), float(factor), int(min_capacity)))
 
 
 @dataclass
@@ -261,16 +268,20 @@ class Layer:
     stores bf16 expert weights (routed and shared) in the packed layout: they are
     reordered once here, into new tensors (the caller's tensors are left as they are).
     prepacked=True: the expert weights given are already packed (pack_weights).
+    capacity_factor: if given, the capacity of each call is capacity_rule(T, k, E,
+    capacity_factor, min_capacity) for its T tokens (instead of the fixed `capacity`).
     """
 
     def __init__(self, w_r, w_gate, w_up, w_down, k, act="swiglu", bias=None, capacity=0,
                  s_gate=None, s_up=None, s_down=None, out_dtype=torch.float32, stats=False,
                  lambda_balance=0.01, lambda_aux=0.01, gamma_aux=100.0, weights="renormalized",
-                 priority="token", overflow="drop", packed=False, prepacked=False):
+                 priority="token", overflow="drop", packed=False, prepacked=False, capacity_factor=None,
+                 min_capacity=0):
         self.w_r, self.bias = w_r, bias
         self.w_gate, self.w_up, self.w_down = w_gate, w_up, w_down
         self.s_gate, self.s_up, self.s_down = s_gate, s_up, s_down
         self.k, self.capacity = k, int(capacity)
+        self.capacity_factor, self.min_capacity = capacity_factor, int(min_capacity)
         if out_dtype not in (torch.float32, torch.bfloat16):
             raise TypeError("out_dtype must be float32 or bfloat16")
         self.out_dtype = out_dtype
@@ -303,7 +314,9 @@ class Layer:
         a.priority = self.priority
         a.overflow = self.overflow
         a.layout = self.layout
-        a.T, a.d, a.F, a.E, a.k, a.capacity = T, self.d, self.F, self.E, self.k, self.capacity
+        a.T, a.d, a.F, a.E, a.k = T, self.d, self.F, self.E, self.k
+        a.capacity = (self.capacity if self.capacity_factor is None else
+                      capacity_rule(T, self.k, self.E, self.capacity_factor, self.min_capacity))
         a.x, a.w_r, a.bias = _ptr(x), _ptr(self.w_r), _ptr(self.bias)
         a.w_gate, a.w_up, a.w_down = _ptr(self.w_gate), _ptr(self.w_up), _ptr(self.w_down)
         a.s_gate, a.s_up, a.s_down = _ptr(self.s_gate), _ptr(self.s_up), _ptr(self.s_down)

@@ -3,6 +3,7 @@
 // ([mlqm] §4.2 forward steps 1-4; [200B-5] "谁来决定请哪几个专家？" and "共享专家…").
 #include "moe_common.h"
 
+#include <cmath>
 #include <mutex>
 #include <map>
 #include <utility>
@@ -143,6 +144,15 @@ moe_status_t moe_route(const void* x, const void* w_r, const float* bias, moe_dt
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(MOE_EWORKSPACE, "route needs %zu workspace bytes, got %zu", need, ws_bytes);
   return launch_route(x, w_r, bias, dt, T, d, E, k, weights, topk_idx, topk_w, logits, ws, stream);
+}
+
+int64_t moe_capacity(int64_t T, int32_t k, int32_t E, double factor, int64_t min_capacity) {
+  if (T < 0 || k < 1 || E < 1 || !std::isfinite(factor)) return 0;
+  constexpr int64_t kMax = (int64_t{1} << 31) - 1;
+  const double q = std::ceil(factor * static_cast<double>(T) * static_cast<double>(k) / static_cast<double>(E));
+  const int64_t c = q >= static_cast<double>(kMax) ? kMax : (q <= -static_cast<double>(kMax) ? -kMax : static_cast<int64_t>(q));
+  const int64_t r = c > min_capacity ? c : min_capacity;
+  return r > kMax ? kMax : r;
 }
 
 size_t moe_dispatch_workspace_bytes(int64_t T, int32_t E, int32_t k) {

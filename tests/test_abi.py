@@ -42,6 +42,25 @@ def test_library_exports_every_declared_symbol(lib):
         assert getattr(lib, n) is not None
 
 
+def test_capacity_helper_matches_the_oracle_rule(lib):
+    """moe_capacity is host logic: the same rule as the oracle's capacity_rule."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    assert lib.moe_capacity(1024, 2, 16, 1.0, 0) == 128                     # (1024x2)/16
+    assert lib.moe_capacity(1024, 2, 16, 1.2, 4) == 154
+    assert lib.moe_capacity(1024, 2, 16, 2.0, 4) == 256
+    assert lib.moe_capacity(1, 2, 16, 1.2, 4) == 4                          # the floor
+    rng = np.random.default_rng(5)
+    for _ in range(2000):
+        T, k, E = int(rng.integers(0, 20000)), int(rng.integers(1, 9)), int(rng.integers(1, 400))
+        f, m = float(rng.choice([0.5, 0.6, 1.0, 1.1, 1.2, 1.25, 2.0, rng.uniform(0.1, 4)])), int(rng.integers(0, 8))
+        assert lib.moe_capacity(T, k, E, f, m) == O.capacity_rule(T, k, E, f, m), (T, k, E, f, m)
+    assert lib.moe_capacity(-1, 2, 16, 1.0, 0) == 0                         # invalid: unlimited
+    assert lib.moe_capacity(16, 0, 16, 1.0, 0) == 0
+    assert lib.moe_capacity(16, 2, 16, float("nan"), 0) == 0
+    assert lib.moe_capacity(1 << 40, 8, 1, 1e6, 0) == (1 << 31) - 1         # clamped
+
+
 def test_status_strings(lib):
     for s, name in B.STATUS.items():
         assert lib.moe_status_string(s).decode().startswith(name)

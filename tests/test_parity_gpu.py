@@ -304,6 +304,30 @@ def test_tile_overrides_against_oracle(tile, monkeypatch):
     _run_and_check(cfg, synth.make_inputs(cfg, DEV), packed=True)
 
 
+def test_layer_capacity_factor():
+    """Layer(capacity_factor, min_capacity) takes each batch's capacity from moe_capacity:
+    the same bits as the explicit capacity the oracle's rule gives, at three batch sizes
+    (the smallest on the floor); one of them also against the oracle."""
+    base = SMALL["bf16-capacity"]
+    inp = synth.make_inputs(base, DEV)
+    for T, f, m in ((400, 0.75, 4), (37, 1.2, 4), (5, 1.2, 4)):
+        C = O.capacity_rule(T, base.k, base.E, f, m)
+        cfg = base.scaled(T=T, capacity=C)
+        sub = dict(inp)
+        sub["x"] = inp["x"][:T].contiguous()
+        Lf = B.Layer(inp["w_r"], inp["w_gate"], inp["w_up"], inp["w_down"], base.k, act=base.act,
+                     bias=inp["bias"], capacity_factor=f, min_capacity=m, packed=True)
+        got = Lf(sub["x"]).clone()
+        nd = int(Lf.n_dropped.item())
+        want = layer_for(cfg, sub)(sub["x"])
+        torch.cuda.synchronize()
+        say(f"[case] capacity factor {f} floor {m} at T={T}: C={C}, dropped {nd}")
+        assert torch.equal(got.view(torch.int32), want.view(torch.int32))
+        if T == 400:
+            assert nd > 0
+            _run_and_check(cfg, sub)
+
+
 def test_deterministic_bits():
     cfg = SMALL["bf16-shared-bias"]
     inp = synth.make_inputs(cfg, DEV)
