@@ -40,6 +40,10 @@
  *     (MOE_EUNSUPPORTED otherwise).  Pointers must be 16-byte aligned.
  *   - Calls on the same stream are ordered; concurrent calls on different streams
  *     share no library state.
+ *   - Graph capture: the compute calls enqueue kernels only (no allocation, memset,
+ *     copy or synchronisation), so they can be captured into a HIP graph on the
+ *     caller's stream.  Make one uncaptured call with the same sizes first: the first
+ *     call of a size may set a kernel's dynamic-LDS attribute (a host-side call).
  */
 #ifndef MOE_H
 #define MOE_H

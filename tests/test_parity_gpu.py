@@ -328,6 +328,32 @@ def test_layer_capacity_factor():
             _run_and_check(cfg, sub)
 
 
+@pytest.mark.parametrize("name", ["bf16-decode", "bf16-capacity-reroute", "bf16-shared-bias"])
+def test_layer_graph_replay(name):
+    """A layer forward captured in a HIP graph: every replay, with new inputs copied into
+    the captured buffer and eager work between replays, gives the eager result's bits."""
+    cfg = SMALL[name]
+    inp = synth.make_inputs(cfg, DEV)
+    L = layer_for(cfg, inp, packed=True)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(cfg.seed)
+    xs = [inp["x"], torch.randn(inp["x"].shape, generator=gen, device=DEV).to(inp["x"].dtype)]
+    eager = [L(x).clone() for x in xs]                 # also sizes the layer's buffers
+    x_static = xs[0].clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = L(x_static)
+    other = layer_for(cfg, inp)                        # eager work between replays
+    for i in (1, 0, 1, 1, 0):
+        x_static.copy_(xs[i])
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"[case] graph replay {cfg.label} input {i}")
+        assert torch.equal(out.view(torch.int32), eager[i].view(torch.int32)), i
+        _ = other(xs[1 - i]).sum().item()
+
+
 def test_deterministic_bits():
     cfg = SMALL["bf16-shared-bias"]
     inp = synth.make_inputs(cfg, DEV)
