@@ -25,6 +25,8 @@
 // router-chosen rows of an expert first and its re-routed arrivals after them.
 #include "moe_common.h"
 
+#include <type_traits>
+
 namespace moe {
 namespace {
 
@@ -111,19 +113,7 @@ __device__ void scatter_block(const int32_t* __restrict__ idx, SlotMap m, int E,
   const int64_t u = static_cast<int64_t>(blockIdx.x) * DP_TOK + threadIdx.x;
   const bool valid = u < m.ntok();
   const int kv = m.kv();
-  for (int j = 0; j < kv; ++j) {
-    int32_t e = valid ? idx[m.slot(u, j)] : -1;
-    if (static_cast<uint32_t>(e) >= static_cast<uint32_t>(E)) e = -1;   // ignored slot
-    // lanes below me (earlier virtual tokens of this wave) that selected e in any of
-    // their slots; a token never selects one expert twice
-    int32_t rank = 0;
-    for (int j2 = 0; j2 < kv; ++j2) {
-      const int32_t v = valid ? idx[m.slot(u, j2)] : -2;
-      for (int src = 0; src < 64; ++src) {
-        const int32_t es = __shfl(v, src);
-        rank += (src < lane && es == e) ? 1 : 0;
-      }
-    }
+  auto place = [&](int j, int32_t e, int32_t rank) {
     if (valid && e < 0) inv[m.slot(u, j)] = -1;
     if (e >= 0) {
       int32_t r = block_base(e) + rank;
@@ -137,6 +127,51 @@ __device__ void scatter_block(const int32_t* __restrict__ idx, SlotMap m, int E,
         inv[slot] = row;
       }
     }
+  };
+  // rank of slot j inside its expert e among this wave's slots: the lanes below me
+  // (earlier virtual tokens) that selected e in any of their slots (a token never
+  // selects one expert twice).  Up to KMAX slots per virtual token, each lane's choices
+  // stay in registers and every (slot, source lane) value is shuffled once for all of
+  // this lane's slots: k*64 shuffles instead of k*k*64 (instantiated for 1, 2, 4 and 8
+  // slots; more take the plain loop).
+  auto fast = [&](auto kmax) {
+    constexpr int KMAX = decltype(kmax)::value;
+    int32_t e[KMAX], raw[KMAX], rank[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      raw[j] = (j < kv && valid) ? idx[m.slot(u, j)] : -2;
+      e[j] = (j < kv && static_cast<uint32_t>(raw[j]) < static_cast<uint32_t>(E)) ? raw[j] : -1;
+      rank[j] = 0;
+    }
+#pragma unroll
+    for (int j2 = 0; j2 < KMAX; ++j2) {
+      if (j2 >= kv) break;
+      for (int src = 0; src < 64; ++src) {
+        const int32_t es = __shfl(raw[j2], src);
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) rank[j] += (src < lane && es == e[j]) ? 1 : 0;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (j < kv) place(j, e[j], rank[j]);
+  };
+  if (kv <= 1) return fast(std::integral_constant<int, 1>());
+  if (kv <= 2) return fast(std::integral_constant<int, 2>());
+  if (kv <= 4) return fast(std::integral_constant<int, 4>());
+  if (kv <= 8) return fast(std::integral_constant<int, 8>());
+  for (int j = 0; j < kv; ++j) {
+    int32_t e = valid ? idx[m.slot(u, j)] : -1;
+    if (static_cast<uint32_t>(e) >= static_cast<uint32_t>(E)) e = -1;   // ignored slot
+    int32_t rank = 0;
+    for (int j2 = 0; j2 < kv; ++j2) {
+      const int32_t v = valid ? idx[m.slot(u, j2)] : -2;
+      for (int src = 0; src < 64; ++src) {
+        const int32_t es = __shfl(v, src);
+        rank += (src < lane && es == e) ? 1 : 0;
+      }
+    }
+    place(j, e, rank);
   }
 }
 
