@@ -596,6 +596,7 @@ __global__ __launch_bounds__(1024) void reroute_list_kernel(const int32_t* __res
 // always succeeds, so every round makes progress.  Same-token entries are adjacent in
 // token-major order (checked k-1 lanes back); in slot-major order a run stops where the
 // slot position changes, and within one slot position the tokens are distinct.
+template <int EM>   // experts held per lane: E <= EM <= 64
 __global__ __launch_bounds__(64) void reroute64_kernel(const int32_t* __restrict__ idx,
                                                        const float* __restrict__ logits, SlotMap m, int E,
                                                        int64_t capacity, const int32_t* __restrict__ ovl,
@@ -625,10 +626,10 @@ __global__ __launch_bounds__(64) void reroute64_kernel(const int32_t* __restrict
     const bool has = c0 + lane < n_over;
     const int32_t slot = has ? ovl[c0 + lane] : 0;
     const int32_t tok = slot / k, jj = slot - (slot / k) * k;
-    float z[64];
+    float z[EM];
     uint64_t tk = 0;
 #pragma unroll
-    for (int e = 0; e < 64; ++e) z[e] = (has && e < E) ? logits[static_cast<int64_t>(tok) * E + e] : 0.f;
+    for (int e = 0; e < EM; ++e) z[e] = (has && e < E) ? logits[static_cast<int64_t>(tok) * E + e] : 0.f;
     for (int q = 0; q < k; ++q) {
       const int32_t eq = has ? idx[static_cast<int64_t>(tok) * k + q] : -1;
       if (static_cast<uint32_t>(eq) < static_cast<uint32_t>(E)) tk |= uint64_t{1} << eq;
@@ -637,18 +638,34 @@ __global__ __launch_bounds__(64) void reroute64_kernel(const int32_t* __restrict
     while (pending) {
       const uint64_t avail = __ballot(lane < E && room > 0) & emask;
       const bool mine = (pending >> lane) & 1;
-      int32_t pick = -1;
-      if (mine) {
-        const uint64_t cand = avail & ~(tk | tused[tok]);
+      const uint64_t used = mine ? tused[tok] : 0;
+      auto best_of = [&](uint64_t cand) {
+        int32_t p = -1;
         float best = 0.f;
 #pragma unroll
-        for (int e = 0; e < 64; ++e) {
+        for (int e = 0; e < EM; ++e) {
           if ((cand >> e) & 1) {
-            if (pick < 0 || z[e] > best) {
+            if (p < 0 || z[e] > best) {
               best = z[e];
-              pick = e;
+              p = e;
             }
           }
+        }
+        return p;
+      };
+      int32_t pick = mine ? best_of(avail & ~(tk | used)) : -1;
+      if (!m.slot_major) {
+        // a token's overflowed slots are adjacent: each slot also excludes the picks of
+        // its token's earlier slots in this run (what it would see after them, if they
+        // are taken in this run; if not, it is past the run's end anyway); k-1 passes
+        // settle a chain of k slots
+        for (int it = 1; it < k && it < 64; ++it) {
+          uint64_t excl = 0;
+          for (int d = 1; d < k && d < 64; ++d) {
+            const int32_t tu = __shfl_up(tok, d), pu = __shfl_up(pick, d);
+            if (lane >= d && ((pending >> (lane - d)) & 1) && tu == tok && pu >= 0) excl |= uint64_t{1} << pu;
+          }
+          if (mine) pick = best_of(avail & ~(tk | used | excl));
         }
       }
       // rank among earlier lanes of the run with the same pick, per distinct pick
@@ -782,9 +799,15 @@ moe_status_t launch_dispatch(const int32_t* topk_idx, const float* logits, int64
     reroute_list_kernel<<<1, 1024, 0, s>>>(topk_idx, inv, m, E, target, ovl, n_over);
     if (moe_status_t st = check_launch("dispatch overflow-list kernel")) return st;
     const size_t lds = static_cast<size_t>(T) * sizeof(uint64_t);
-    set_max_dynamic_smem(reinterpret_cast<const void*>(reroute64_kernel), lds);
-    reroute64_kernel<<<1, 64, lds, s>>>(topk_idx, logits, m, E, capacity, ovl, n_over, offsets, off1, target,
-                                        arrival, n_dropped);
+    auto run = [&](auto kern) {
+      set_max_dynamic_smem(reinterpret_cast<const void*>(kern), lds);
+      kern<<<1, 64, lds, s>>>(topk_idx, logits, m, E, capacity, ovl, n_over, offsets, off1, target, arrival,
+                              n_dropped);
+    };
+    // the per-round argmax and the logit row cover EM experts per lane
+    if (E <= 16) run(reroute64_kernel<16>);
+    else if (E <= 32) run(reroute64_kernel<32>);
+    else run(reroute64_kernel<64>);
     if (moe_status_t st = check_launch("dispatch re-route kernel")) return st;
     dispatch_rebuild_kernel<<<static_cast<unsigned>((nslots + 255) / 256), 256, 0, s>>>(
         topk_idx, nslots, E, off1, offsets, target, arrival, perm, inv);

@@ -378,12 +378,14 @@ def test_empty_batch_is_noop():
 # ---- the five workloads at full size (routing on every token, outputs sampled) ----
 # sampled output tokens per full-size workload (None: every token)
 SAMPLES = {"prefill-e64": 8, "shared-routed-e16": 10, "capacity-e16": 12, "decode-e64": None,
-           "capacity-e16-slot-reroute": 12, "wide-e384-top6-shared": 4, "wide-e128-top2": 8}
+           "capacity-e16-slot-reroute": 12, "capacity-e16-reroute": 12, "wide-e384-top6-shared": 4, "wide-e128-top2": 8}
 FULL = {n: BY_NAME[n] for n in ("prefill-e64", "shared-routed-e16", "capacity-e16", "decode-e64",
                                 "wide-e384-top6-shared", "wide-e128-top2")}
 # the capacity workload with first choices first and overflow re-routed
 FULL["capacity-e16-slot-reroute"] = BY_NAME["capacity-e16"].scaled(name="capacity-e16-slot-reroute",
                                                                    priority="slot", overflow="reroute")
+# and with token-major priority (a token's overflowed slots are adjacent in the list)
+FULL["capacity-e16-reroute"] = BY_NAME["capacity-e16"].scaled(name="capacity-e16-reroute", overflow="reroute")
 
 
 @pytest.mark.parametrize("name", list(FULL))
