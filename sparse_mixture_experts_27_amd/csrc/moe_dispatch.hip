@@ -594,8 +594,10 @@ __global__ __launch_bounds__(1024) void reroute_list_kernel(const int32_t* __res
 // (room only shrinks and a token's excluded set only grows), so the run up to the first
 // pick that fails this is applied at once and the rest pick again; the first pending lane
 // always succeeds, so every round makes progress.  Same-token entries are adjacent in
-// token-major order (checked k-1 lanes back); in slot-major order a run stops where the
-// slot position changes, and within one slot position the tokens are distinct.
+// token-major order: each re-picks (k-1 passes) with the picks of its token's earlier
+// entries in the run added to its mask, which is the choice it would face after them, and
+// a same-expert pick within k-1 lanes still ends the run; in slot-major order a run stops
+// where the slot position changes, and within one slot position the tokens are distinct.
 template <int EM>   // experts held per lane: E <= EM <= 64
 __global__ __launch_bounds__(64) void reroute64_kernel(const int32_t* __restrict__ idx,
                                                        const float* __restrict__ logits, SlotMap m, int E,
