@@ -36,7 +36,8 @@
  *     bf16 once.  MOE_F32: everything is fp32.  Logits, routing weights and the
  *     per-row expert outputs y are always fp32.
  *   - Requirements: T >= 0 (T == 0 is a no-op), d >= 1, 1 <= E <= 1024,
- *     1 <= k <= E, F >= 1; for MOE_BF16 expert FFNs, d and F must be multiples of 64
+ *     1 <= k <= E, F >= 1; for MOE_BF16 expert FFNs, d and F must be multiples of 64,
+ *     and MOE_BF16 routing with d not a multiple of 32 takes at most 888 experts
  *     (MOE_EUNSUPPORTED otherwise).  Pointers must be 16-byte aligned.
  *   - Calls on the same stream are ordered; concurrent calls on different streams
  *     share no library state.

@@ -71,6 +71,10 @@ moe_status_t check_route_args(const void* x, const void* w_r, int dt, int64_t T,
   if (E < 1 || E > kMaxExperts) return fail(MOE_EINVAL, "E=%d must be in [1, %d]", E, kMaxExperts);
   if (k < 1 || k > E) return fail(MOE_EINVAL, "k=%d must be in [1, E=%d]", k, E);
   if (T * k > (int64_t{1} << 31) - 1) return fail(MOE_EINVAL, "T*k exceeds 2^31-1");
+  if (route_lds_bytes(d, E, dt) > kMaxLdsBytes)
+    return fail(MOE_EUNSUPPORTED, "routing %d experts with d=%lld needs %zu bytes of LDS per workgroup (most %zu); "
+                "bf16 routing with d not a multiple of 32 supports at most 888 experts",
+                E, (long long)d, route_lds_bytes(d, E, dt), kMaxLdsBytes);
   if (T > 0 && (!x || !w_r || !topk_idx || !topk_w || !logits))
     return fail(MOE_EINVAL, "moe_route: null required pointer");
   if (T > 0 && (!aligned16(x) || !aligned16(w_r))) return fail(MOE_EINVAL, "x and w_r must be 16-byte aligned");

@@ -45,6 +45,9 @@ struct WsCarver {
 // The router splits K over workgroups when there are few token blocks; ws holds the
 // partial logits (route_ws_bytes; 0 when no split is used).
 size_t route_ws_bytes(int64_t T, int64_t d, int E, int dt);
+// Dynamic LDS bytes the routing kernels request for these sizes (at most kMaxLdsBytes).
+size_t route_lds_bytes(int64_t d, int E, int dt);
+constexpr size_t kMaxLdsBytes = 160 * 1024;   // LDS of one gfx950 CU, the most one workgroup can use
 moe_status_t launch_route(const void* x, const void* w_r, const float* bias, int dt,
                           int64_t T, int64_t d, int E, int k, int mode, int32_t* topk_idx,
                           float* topk_w, float* logits, void* ws, hipStream_t s);

@@ -25,15 +25,17 @@ constexpr int RT_PITCH = RT_KC + 8;   // LDS row pitch (elements) of the transpo
 
 // Dynamic LDS layout; the logit rows are sized by E, so E <= 64 stays under 64 KB.
 struct RouteSmem {
-  uint16_t (*wt)[RT_PITCH];   // [RT_EB][RT_PITCH]  W_r chunk, [expert][k]   (bf16 path)
-  float (*red)[RT_TOK][RT_EB];// [4][RT_TOK][RT_EB] per-wave partial logits (bf16 path)
+  uint16_t (*wt)[RT_PITCH];   // [RT_EB][RT_PITCH]  W_r chunk, [expert][k]   (LDS-staged bf16 path)
+  float (*red)[RT_TOK][RT_EB];// [4][RT_TOK][RT_EB] per-wave partial logits (bf16 paths)
   float* z;                   // [RT_TOK][E]        final logits of the 16 tokens
   float* zs;                  // [RT_TOK][E]        selected logits, one row per token
-  __device__ RouteSmem(char* base, int E, bool gemm) {
+  __device__ RouteSmem(char* base, int E, bool wt_buf, bool red_buf) {
     size_t off = 0;
-    if (gemm) {
+    if (wt_buf) {
       wt = reinterpret_cast<uint16_t(*)[RT_PITCH]>(base);
       off += sizeof(uint16_t) * RT_EB * RT_PITCH;
+    }
+    if (red_buf) {
       red = reinterpret_cast<float(*)[RT_TOK][RT_EB]>(base + off);
       off += sizeof(float) * 4 * RT_TOK * RT_EB;
     }
@@ -43,9 +45,10 @@ struct RouteSmem {
   }
 };
 
-inline size_t route_smem_bytes(int E, bool gemm) {
+inline size_t route_smem_bytes(int E, bool wt_buf, bool red_buf) {
   size_t b = sizeof(float) * (2 * RT_TOK) * static_cast<size_t>(E);
-  if (gemm) b += sizeof(uint16_t) * RT_EB * RT_PITCH + sizeof(float) * 4 * RT_TOK * RT_EB;
+  if (wt_buf) b += sizeof(uint16_t) * RT_EB * RT_PITCH;
+  if (red_buf) b += sizeof(float) * 4 * RT_TOK * RT_EB;
   return b;
 }
 
@@ -154,7 +157,7 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
     int64_t T, int64_t d, int E, int k, int mode, int64_t kchunk, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, float* __restrict__ logits, float* __restrict__ partial) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  RouteSmem sm(smem_raw, E, true);
+  RouteSmem sm(smem_raw, E, true, true);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * RT_TOK;
   const bool split = gridDim.y > 1;
@@ -283,7 +286,7 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(
     int64_t T, int64_t d, int E, int Ep, int k, int mode, int64_t kchunk, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, float* __restrict__ logits, float* __restrict__ partial) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  RouteSmem sm(smem_raw, E, true);
+  RouteSmem sm(smem_raw, E, false, true);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * RT_TOK;
   const bool split = gridDim.y > 1;
@@ -371,7 +374,7 @@ __global__ __launch_bounds__(256) void route_finish_kernel(const float* __restri
                                                            int k, int mode, int32_t* __restrict__ topk_idx,
                                                            float* __restrict__ topk_w, float* __restrict__ logits) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  RouteSmem sm(smem_raw, E, false);
+  RouteSmem sm(smem_raw, E, false, false);
   const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * RT_TOK;
   for (int i = threadIdx.x; i < RT_TOK * E; i += 256) {
     const int t = i / E, e = i % E;
@@ -402,7 +405,7 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
     int64_t T, int64_t d, int E, int k, int mode, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     float* __restrict__ logits) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  RouteSmem sm(smem_raw, E, false);
+  RouteSmem sm(smem_raw, E, false, false);
   const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * RT_TOK;
   for (int i = threadIdx.x; i < RT_TOK * E; i += 256) {
     const int t = i / E, e = i % E;
@@ -439,6 +442,12 @@ size_t route_wt_bytes(int64_t d, int E, int dt) {
   return route_direct(d, dt) ? align_up(static_cast<size_t>(route_padded_experts(E)) * d * sizeof(uint16_t), 256) : 0;
 }
 
+size_t route_lds_bytes(int64_t d, int E, int dt) {
+  // the largest dynamic LDS request of the routing kernels for these sizes
+  if (dt != MOE_BF16) return route_smem_bytes(E, false, false);
+  return route_smem_bytes(E, !route_direct(d, dt), true);
+}
+
 size_t route_ws_bytes(int64_t T, int64_t d, int E, int dt) {
   const int ks = route_splits(T, d, dt);
   return route_wt_bytes(d, E, dt) + (ks > 1 ? static_cast<size_t>(ks) * T * E * sizeof(float) : 0);
@@ -453,7 +462,7 @@ moe_status_t launch_route(const void* x, const void* w_r, const float* bias, int
     const int ks = route_splits(T, d, dt);
     const int64_t chunks = (d + RT_KC - 1) / RT_KC;
     const int64_t kchunk = ((chunks + ks - 1) / ks) * RT_KC;
-    const size_t smem = route_smem_bytes(E, true);
+    const size_t smem = route_smem_bytes(E, !route_direct(d, dt), true);
     const size_t wtb = route_wt_bytes(d, E, dt);
     float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + wtb);
     if (route_direct(d, dt)) {
@@ -473,14 +482,14 @@ moe_status_t launch_route(const void* x, const void* w_r, const float* bias, int
     }
     if (moe_status_t st = check_launch("route kernel")) return st;
     if (ks > 1) {
-      const size_t smem2 = route_smem_bytes(E, false);
+      const size_t smem2 = route_smem_bytes(E, false, false);
       set_max_dynamic_smem(reinterpret_cast<const void*>(route_finish_kernel), smem2);
       route_finish_kernel<<<grid, 256, smem2, s>>>(partial, ks, bias, T, E, k, mode, topk_idx, topk_w, logits);
       return check_launch("route finish kernel");
     }
     return MOE_OK;
   }
-  const size_t smem = route_smem_bytes(E, false);
+  const size_t smem = route_smem_bytes(E, false, false);
   set_max_dynamic_smem(reinterpret_cast<const void*>(route_f32_kernel), smem);
   route_f32_kernel<<<grid, 256, smem, s>>>(static_cast<const float*>(x), static_cast<const float*>(w_r), bias, T,
                                            d, E, k, mode, topk_idx, topk_w, logits);

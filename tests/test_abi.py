@@ -78,6 +78,11 @@ def test_route_validation(lib):
     assert _route(lib, k=0) == 1
     assert _route(lib, k=9) == 1
     assert b"k=9" in lib.moe_last_error()
+    # bf16 routing through the LDS-staged path (d % 32 != 0) holds at most 888 experts
+    assert _route(lib, d=200, E=889, k=2) == 2
+    assert b"888" in lib.moe_last_error()
+    assert _route(lib, d=200, E=888, k=2, x=0, idx=0) == 1            # size accepted, then null pointers
+    assert _route(lib, d=256, E=1024, k=2, x=0, idx=0) == 1           # d % 32 == 0: 1024 experts fit
     assert _route(lib, E=0) == 1
     assert _route(lib, E=1025) == 1
     assert _route(lib, dt=7) == 1

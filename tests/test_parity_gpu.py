@@ -39,6 +39,9 @@ SMALL = {
     "bf16-e128-top2": MoEConfig("bf16-e128", 21, T=200, d=128, E=128, k=2, F=128, act="swiglu", dtype="bf16"),
     "bf16-e384-top6-shared": MoEConfig("bf16-e384", 22, T=96, d=128, E=384, k=6, F=64, act="swiglu",
                                        dtype="bf16", shared=True),
+    # the largest expert count the library accepts
+    "bf16-e1024-top8": MoEConfig("bf16-e1024", 24, T=256, d=64, E=1024, k=8, F=64, act="swiglu", dtype="bf16",
+                                 bias_var=0.5),
     "bf16-capacity-one": MoEConfig("bf16-c1", 23, T=64, d=128, E=4, k=2, F=64, act="swiglu", dtype="bf16",
                                    capacity=1),
     # routing weights = the selected softmax probabilities, not renormalised
@@ -136,7 +139,7 @@ def test_worked_example_on_gpu():
 
 
 @pytest.mark.parametrize("T,d,E,k", [(37, 200, 12, 3), (600, 200, 40, 2), (600, 224, 12, 2), (5, 4096, 70, 4),
-                                     (300, 512, 130, 6)])
+                                     (300, 512, 130, 6), (64, 256, 1024, 8), (3, 128, 1024, 1024)])
 def test_route_shapes(T, d, E, k):
     """moe_route alone on shapes the layers above do not reach: d not a multiple of 32
     (W_r staged through LDS), E not a multiple of 16 (padded expert blocks), more than
@@ -156,6 +159,7 @@ def test_route_shapes(T, d, E, k):
 
 @pytest.mark.parametrize("T,E,k,C", [(1, 4, 2, 1), (37, 5, 2, 4), (300, 8, 2, 40), (600, 16, 3, 70),
                                      (129, 64, 6, 9), (200, 32, 10, 50), (513, 6, 1, 50), (40, 1000, 300, 8),
+                                     (300, 1024, 4, 2),
                                      (100, 1, 1, 10), (64, 2, 2, 5), (12000, 16, 2, 1600), (20000, 16, 2, 2600)])
 def test_dispatch_policies(T, E, k, C):
     """moe_dispatch alone, every priority x overflow pair, bit-exact against the oracle
