@@ -132,8 +132,9 @@ __device__ void scatter_block(const int32_t* __restrict__ idx, SlotMap m, int E,
   // (earlier virtual tokens) that selected e in any of their slots (a token never
   // selects one expert twice).  Up to KMAX slots per virtual token, each lane's choices
   // stay in registers and every (slot, source lane) value is shuffled once for all of
-  // this lane's slots: k*64 shuffles instead of k*k*64 (instantiated for 1, 2, 4 and 8
-  // slots; more take the plain loop).
+  // this lane's slots: k*64 lane reads instead of k*k*64 (instantiated for 1, 2, 4 and 8
+  // slots; more take the plain loop).  The source lane is a loop counter, the same in
+  // every lane, so a scalar lane read does the job (every lane of the block is active).
   auto fast = [&](auto kmax) {
     constexpr int KMAX = decltype(kmax)::value;
     int32_t e[KMAX], raw[KMAX], rank[KMAX];
@@ -147,7 +148,7 @@ __device__ void scatter_block(const int32_t* __restrict__ idx, SlotMap m, int E,
     for (int j2 = 0; j2 < KMAX; ++j2) {
       if (j2 >= kv) break;
       for (int src = 0; src < 64; ++src) {
-        const int32_t es = __shfl(raw[j2], src);
+        const int32_t es = __builtin_amdgcn_readlane(raw[j2], src);   // uniform source lane
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) rank[j] += (src < lane && es == e[j]) ? 1 : 0;
       }
@@ -167,7 +168,7 @@ __device__ void scatter_block(const int32_t* __restrict__ idx, SlotMap m, int E,
     for (int j2 = 0; j2 < kv; ++j2) {
       const int32_t v = valid ? idx[m.slot(u, j2)] : -2;
       for (int src = 0; src < 64; ++src) {
-        const int32_t es = __shfl(v, src);
+        const int32_t es = __builtin_amdgcn_readlane(v, src);
         rank += (src < lane && es == e) ? 1 : 0;
       }
     }
