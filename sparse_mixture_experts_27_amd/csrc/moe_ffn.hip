@@ -13,9 +13,10 @@
 // bf16 tile: up to 256 rows x 256 MFMA columns x 64 K per stage, 8 waves (2 per SIMD).
 // Wave w owns 32 columns of every row of the tile: its weight fragments are private to
 // it and are loaded straight from global memory into registers in the MFMA operand
-// layout (no LDS), while the activation tile is shared by the 8 waves through a ring of
-// 3 LDS slots, written by buffer-to-LDS loads (no register round trip), 16-byte chunks
-// XOR-swizzled by row.  Only the 16-row fragments that hold real rows are multiplied,
+// layout (no LDS; in the packed weight layout each such load reads one contiguous KiB),
+// while the activation tile is shared by the 8 waves through a ring of 3 LDS slots,
+// written by buffer-to-LDS loads (no register round trip), 16-byte chunks XOR-swizzled
+// by row.  Only the 16-row fragments that hold real rows are multiplied,
 // so a group with 70 rows costs 5 fragments, not 16.  Workgroups are remapped so that
 // each XCD (blockIdx % 8) walks a contiguous range of tiles: the tiles of one expert
 // share its activation rows in that XCD's L2.
