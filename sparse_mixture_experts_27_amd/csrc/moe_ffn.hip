@@ -353,6 +353,25 @@ __device__ __forceinline__ void ffn_gemm_bf16_body(const GemmArgs& p, uint16_t* 
         rb[slot][s][nf] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, boff[nf] + s * W_STEP, ko, 0));
       }
   };
+  // One load of a phase by index, in the phase's issue order: the AR activation chunks of
+  // stage sta, then the 2*NF weight fragments of stage stb (k32 step major).
+  auto load_one = [&](int idx, int sta, int lslot, int stb, int bslot) {
+    if (idx < AR) {
+      const int ko = clamp_stage(sta) * (BK * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc,
+          (__attribute__((address_space(3))) void*)(lds(lslot) + (idx * (NT / 64) + wave) * 512), 16, aoff[idx], ko,
+          0, 0);
+    } else {
+      const int w = idx - AR, s = w / NF, nf = w % NF;
+      const int ko = clamp_stage(stb) * W_STAGE;
+      if (PAIRED) {
+        rb[bslot][s][0] = *reinterpret_cast<const bf16x8*>(wlane + ko + s * W_STEP);
+      } else {
+        const auto& rs = (MODE == MODE_SWIGLU_UP && nf >= NF / 2) ? w1rsrc : w0rsrc;
+        rb[bslot][s][nf] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, boff[nf] + s * W_STEP, ko, 0));
+      }
+    }
+  };
   // Mark a weight slot as consumed on every path (the MFMAs that read it sit behind the
   // row-count guards), so its registers can be reloaded without a memory wait.
   auto consume_b = [&](int slot) {
@@ -381,7 +400,17 @@ __device__ __forceinline__ void ffn_gemm_bf16_body(const GemmArgs& p, uint16_t* 
   constexpr int GS = MT < 4 ? MT : 4;
   constexpr int NG = 2 * (MT / GS);          // groups per stage: 2 k32 steps x MT/GS
   constexpr bool PREFETCH = MT <= 8 || NW <= 8;
-  auto compute = [&](int aslot, int bslot) {
+  // With spread loads, the activation chunks of the next stage go first, in one burst,
+  // and group q then issues weight fragments [q*NW2/NG, (q+1)*NW2/NG) (every path issues
+  // them all), so the memory pipeline takes the weights in while the MFMAs run.  (Loads
+  // into LDS placed between the LDS reads make the compiler wait for nearly all loads in
+  // flight before those reads, so they stay in front.)
+  constexpr int NW2 = 2 * NF;
+  auto compute = [&](int aslot, int bslot, bool spread, int sta, int lslot_n, int stb, int bslot_n) {
+    if (spread) {
+#pragma unroll
+      for (int i = 0; i < AR; ++i) load_one(i, sta, lslot_n, stb, bslot_n);
+    }
     bf16x8 a[PREFETCH ? 2 : 1][GS];
     if (PREFETCH) {
 #pragma unroll
@@ -390,6 +419,10 @@ __device__ __forceinline__ void ffn_gemm_bf16_body(const GemmArgs& p, uint16_t* 
 #pragma unroll
     for (int q = 0; q < NG; ++q) {
       const int s = q / (MT / GS), g = q % (MT / GS);
+      if (spread) {
+#pragma unroll
+        for (int i = q * NW2 / NG; i < (q + 1) * NW2 / NG; ++i) load_one(AR + i, sta, lslot_n, stb, bslot_n);
+      }
       const int cur = PREFETCH ? (q & 1) : 0;
       if (PREFETCH && q + 1 < NG) {
         const int s1 = (q + 1) / (MT / GS), g1 = (q + 1) % (MT / GS);
@@ -440,10 +473,17 @@ __device__ __forceinline__ void ffn_gemm_bf16_body(const GemmArgs& p, uint16_t* 
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     }
   };
+  // Activation loads go to LDS (not the register path) and every phase's loads can be
+  // spread over its MFMA groups.
+  constexpr bool SPREAD = !WRAP;
   auto phase = [&](int st, int ph) {
-    load_a(st + D, pm(ph + D, 2), pm(ph + D, LRING));
-    load_b(st + WRING - 1, pm(ph + WRING - 1, WRING));
-    compute(pm(ph, LRING), pm(ph, WRING));
+    if (SPREAD) {
+      compute(pm(ph, LRING), pm(ph, WRING), true, st + D, pm(ph + D, LRING), st + WRING - 1, pm(ph + WRING - 1, WRING));
+    } else {
+      load_a(st + D, pm(ph + D, 2), pm(ph + D, LRING));
+      load_b(st + WRING - 1, pm(ph + WRING - 1, WRING));
+      compute(pm(ph, LRING), pm(ph, WRING), false, 0, 0, 0, 0);
+    }
     consume_b(pm(ph, WRING));
     store_a(pm(ph + 1, 2), pm(ph + 1, LRING));
     barrier();
