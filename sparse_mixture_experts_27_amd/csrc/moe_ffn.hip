@@ -10,7 +10,8 @@
 // A device-side schedule (one tiny kernel) turns the group offsets into M-tiles, so
 // no host synchronisation is needed to learn how many rows each expert received.
 //
-// bf16 tile: up to 256 rows x 256 MFMA columns x 64 K per stage, 8 waves (2 per SIMD).
+// bf16 tile: up to 256 rows x 256 MFMA columns x 64 K per stage, 8 waves (2 per SIMD)
+// (tile heights 32, 64, 128, 192 and 256 rows).
 // Wave w owns 32 columns of every row of the tile: its weight fragments are private to
 // it and are loaded straight from global memory into registers in the MFMA operand
 // layout (no LDS; in the packed weight layout each such load reads one contiguous KiB),
@@ -666,7 +667,16 @@ __global__ __launch_bounds__(256) void ffn_reduce_splits_kernel(const float* __r
   }
 }
 
-// Launch one bf16 grouped GEMM with the M-tile (MT*16 rows) chosen by the plan.
+// Tile shapes with a bf16 kernel: 32, 64, 128 or 256 rows with 4, 8 or 16 waves, and 192
+// rows with 8 waves (12 row fragments; at 4 or 16 waves that height would need the register
+// path for the activations or more registers than a wave has).
+bool bf16_tile_supported(int bm, int nw) {
+  if (nw != 4 && nw != 8 && nw != 16) return false;
+  return bm == 32 || bm == 64 || bm == 128 || bm == 256 || (bm == 192 && nw == 8);
+}
+
+// Launch one bf16 grouped GEMM with the M-tile (MT*16 rows) chosen by the plan (a shape
+// that bf16_tile_supported accepts; the schedule was built for the same height).
 template <int MODE, bool PK>
 void launch_bf16_gemm_l(int bm, int nw, int64_t grid, const GemmArgs& g, hipStream_t s) {
   const unsigned gr = static_cast<unsigned>(grid);
@@ -675,21 +685,25 @@ void launch_bf16_gemm_l(int bm, int nw, int64_t grid, const GemmArgs& g, hipStre
       case 32: ffn_gemm_bf16_kernel<MODE, 2, 16, PK><<<gr, 1024, 0, s>>>(g); break;
       case 64: ffn_gemm_bf16_kernel<MODE, 4, 16, PK><<<gr, 1024, 0, s>>>(g); break;
       case 128: ffn_gemm_bf16_kernel<MODE, 8, 16, PK><<<gr, 1024, 0, s>>>(g); break;
-      default: ffn_gemm_bf16_kernel<MODE, 16, 16, PK><<<gr, 1024, 0, s>>>(g); break;
+      case 256: ffn_gemm_bf16_kernel<MODE, 16, 16, PK><<<gr, 1024, 0, s>>>(g); break;
+      default: break;
     }
   } else if (nw == 8) {
     switch (bm) {
       case 32: ffn_gemm_bf16_kernel<MODE, 2, 8, PK><<<gr, 512, 0, s>>>(g); break;
       case 64: ffn_gemm_bf16_kernel<MODE, 4, 8, PK><<<gr, 512, 0, s>>>(g); break;
       case 128: ffn_gemm_bf16_kernel<MODE, 8, 8, PK><<<gr, 512, 0, s>>>(g); break;
-      default: ffn_gemm_bf16_kernel<MODE, 16, 8, PK><<<gr, 512, 0, s>>>(g); break;
+      case 192: ffn_gemm_bf16_kernel<MODE, 12, 8, PK><<<gr, 512, 0, s>>>(g); break;
+      case 256: ffn_gemm_bf16_kernel<MODE, 16, 8, PK><<<gr, 512, 0, s>>>(g); break;
+      default: break;
     }
   } else {
     switch (bm) {
       case 32: ffn_gemm_bf16_kernel<MODE, 2, 4, PK><<<gr, 256, 0, s>>>(g); break;
       case 64: ffn_gemm_bf16_kernel<MODE, 4, 4, PK><<<gr, 256, 0, s>>>(g); break;
       case 128: ffn_gemm_bf16_kernel<MODE, 8, 4, PK><<<gr, 256, 0, s>>>(g); break;
-      default: ffn_gemm_bf16_kernel<MODE, 16, 4, PK><<<gr, 256, 0, s>>>(g); break;
+      case 256: ffn_gemm_bf16_kernel<MODE, 16, 4, PK><<<gr, 256, 0, s>>>(g); break;
+      default: break;
     }
   }
 }
@@ -702,11 +716,15 @@ void launch_bf16_gemm(bool packed, int bm, int nw, int64_t grid, const GemmArgs&
 
 }  // namespace
 
-// M-tile height: the smallest of 32/64/128/256 rows that holds a typical routed group in
-// one tile, so each expert's weights stream once.  The rows per group are only known on
+// M-tile height: the smallest of 32/64/128/192/256 rows that holds a typical routed group
+// in one tile, so each expert's weights stream once.  The rows per group are only known on
 // the device; the host estimate is the capacity when one is set, else 1.6x the mean load
-// (plus a margin for small loads).  A shared group (T rows) does not raise it: its M-tiles
-// are adjacent in the schedule and share its weights in L2, while routed experts are the
+// (plus a margin for small loads).  192 rows are taken up to an estimate of 224: the
+// activation loads of a tile cover its full height (padding rows included), and a group
+// over 192 rows costs a second, mostly empty tile whose weights come from L2, which pays
+// while such groups are rare (measured on 64 experts x 128 rows on average: 2% faster
+// than 256-row tiles).  A shared group (T rows) does not raise it: its M-tiles are
+// adjacent in the schedule and share its weights in L2, while routed experts are the
 // bulk of the weight bytes.
 FfnPlan ffn_plan(int64_t max_rows, int G, int64_t shared_rows, int64_t d, int64_t F, int act, int dt,
                  int64_t capacity) {
@@ -718,14 +736,16 @@ FfnPlan ffn_plan(int64_t max_rows, int G, int64_t shared_rows, int64_t d, int64_
     const int64_t routed = max_rows - (has_shared ? shared_rows : 0);
     double est = 1.6 * static_cast<double>(routed) / (G > 0 ? G : 1) + 16.0;
     if (capacity > 0 && static_cast<double>(capacity) < est) est = static_cast<double>(capacity);
-    pl.bm = est <= 32 ? 32 : est <= 64 ? 64 : est <= 128 ? 128 : BM;
-    // tuning override of the tile height (32, 64, 128 or 256 rows)
+    pl.bm = est <= 32 ? 32 : est <= 64 ? 64 : est <= 128 ? 128 : est <= 224 ? 192 : BM;
+    pl.nw = 8;
+    // tuning overrides of the waves per workgroup (4, 8 or 16) and the tile height (32, 64,
+    // 128, 192 or 256 rows); a height without a kernel at that wave count becomes 256
+    if (const char* o = getenv("MOE_TILE_WAVES")) pl.nw = atoi(o) == 4 ? 4 : atoi(o) == 16 ? 16 : 8;
     if (const char* o = getenv("MOE_TILE_ROWS")) {
       const int v = atoi(o);
-      if (v == 32 || v == 64 || v == 128 || v == 256) pl.bm = v;
+      if (v == 32 || v == 64 || v == 128 || v == 192 || v == 256) pl.bm = v;
     }
-    pl.nw = 8;
-    if (const char* o = getenv("MOE_TILE_WAVES")) pl.nw = atoi(o) == 4 ? 4 : atoi(o) == 16 ? 16 : 8;
+    if (!bf16_tile_supported(pl.bm, pl.nw)) pl.bm = BM;
   } else {
     pl.bm = BM_F32;
   }
@@ -769,6 +789,7 @@ moe_status_t launch_ffn(const FfnProblem& p, const FfnPlan& plan, float* y, bool
     mark(0); mark(1); mark(2);
     return MOE_OK;
   }
+  if (bf && !bf16_tile_supported(bm, plan.nw)) return MOE_EINVAL;
 
   ffn_schedule_kernel<<<1, 1024, 0, s>>>(p.offsets, p.G, p.max_rows, p.shared_rows, p.shared_row0, bm, sched);
   if (moe_status_t st = check_launch("ffn schedule kernel")) return st;
