@@ -309,6 +309,48 @@ def test_tile_overrides_against_oracle(tile, monkeypatch):
     _run_and_check(cfg, synth.make_inputs(cfg, DEV), packed=True)
 
 
+# group sizes on both sides of a tile height (and of two tiles), a one-row group and an
+# empty group, for every tile shape the plan can pick
+EDGE_TILES = [("32", "8"), ("64", "8"), ("128", "8"), ("192", "8"), ("256", "8"), ("256", "16"), ("128", "4")]
+
+
+@pytest.mark.parametrize("tile", EDGE_TILES, ids=[f"{t[0]}x{t[1]}" for t in EDGE_TILES])
+def test_group_sizes_around_tile_heights(tile, monkeypatch):
+    """moe_expert_ffn on identity rows with groups of h-1, h, h+1, 1, 0 and 2h+3 rows for
+    tile height h: every row against the oracle's FFN of its group, packed weights bit
+    for bit equal to the nn.Linear layout."""
+    monkeypatch.setenv("MOE_TILE_ROWS", tile[0])
+    monkeypatch.setenv("MOE_TILE_WAVES", tile[1])
+    h = int(tile[0])
+    sizes = [h - 1, h, h + 1, 1, 0, 2 * h + 3]
+    G, d, F = len(sizes), 128, 192
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    R = int(offs[-1])
+    g = torch.Generator().manual_seed(29 + h)
+    x = torch.randn(R, d, generator=g).to(torch.bfloat16)
+    wg = (torch.randn(G, F, d, generator=g) / d ** 0.5).to(torch.bfloat16)
+    wu = (torch.randn(G, F, d, generator=g) / d ** 0.5).to(torch.bfloat16)
+    wd = (torch.randn(G, d, F, generator=g) / F ** 0.5).to(torch.bfloat16)
+    dx, dg, du, dd = (t.to(DEV) for t in (x, wg, wu, wd))
+    off_t = torch.from_numpy(offs).to(DEV)
+    say(f"[case] expert FFN group sizes {sizes} tile={tile}")
+    y = B.expert_ffn(dx, off_t, dg, du, dd, R, act="swiglu").clone()
+    y_p = B.expert_ffn(dx, off_t, B.pack_weights(dg), B.pack_weights(du), B.pack_weights(dd), R, act="swiglu",
+                       packed=True).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(y_p.view(torch.int32), y.view(torch.int32))
+    x64 = x.double().numpy()
+    ref = np.zeros((R, d))
+    for e in range(G):
+        if sizes[e]:
+            r = slice(int(offs[e]), int(offs[e + 1]))
+            ref[r] = O.expert_ffn(x64[r], "swiglu", wg[e].double().numpy(), wu[e].double().numpy(),
+                                  wd[e].double().numpy())
+    got = y.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    assert np.abs(got - ref).max() <= 2e-2 * np.sqrt(np.mean(ref ** 2))
+
+
 def test_layer_capacity_factor():
     """Layer(capacity_factor, min_capacity) takes each batch's capacity from moe_capacity:
     the same bits as the explicit capacity the oracle's rule gives, at three batch sizes
