@@ -314,8 +314,9 @@ def test_tile_overrides_against_oracle(tile, monkeypatch):
 EDGE_TILES = [("32", "8"), ("64", "8"), ("128", "8"), ("192", "8"), ("256", "8"), ("256", "16"), ("128", "4")]
 
 
+@pytest.mark.parametrize("act", ["swiglu", "gelu"])
 @pytest.mark.parametrize("tile", EDGE_TILES, ids=[f"{t[0]}x{t[1]}" for t in EDGE_TILES])
-def test_group_sizes_around_tile_heights(tile, monkeypatch):
+def test_group_sizes_around_tile_heights(tile, act, monkeypatch):
     """moe_expert_ffn on identity rows with groups of h-1, h, h+1, 1, 0 and 2h+3 rows for
     tile height h: every row against the oracle's FFN of its group, packed weights bit
     for bit equal to the nn.Linear layout."""
@@ -333,10 +334,12 @@ def test_group_sizes_around_tile_heights(tile, monkeypatch):
     wd = (torch.randn(G, d, F, generator=g) / F ** 0.5).to(torch.bfloat16)
     dx, dg, du, dd = (t.to(DEV) for t in (x, wg, wu, wd))
     off_t = torch.from_numpy(offs).to(DEV)
-    say(f"[case] expert FFN group sizes {sizes} tile={tile}")
-    y = B.expert_ffn(dx, off_t, dg, du, dd, R, act="swiglu").clone()
-    y_p = B.expert_ffn(dx, off_t, B.pack_weights(dg), B.pack_weights(du), B.pack_weights(dd), R, act="swiglu",
-                       packed=True).clone()
+    if act == "gelu":
+        du = None
+    say(f"[case] expert FFN ({act}) group sizes {sizes} tile={tile}")
+    y = B.expert_ffn(dx, off_t, dg, du, dd, R, act=act).clone()
+    y_p = B.expert_ffn(dx, off_t, B.pack_weights(dg), None if du is None else B.pack_weights(du),
+                       B.pack_weights(dd), R, act=act, packed=True).clone()
     torch.cuda.synchronize()
     assert torch.equal(y_p.view(torch.int32), y.view(torch.int32))
     x64 = x.double().numpy()
@@ -344,7 +347,7 @@ def test_group_sizes_around_tile_heights(tile, monkeypatch):
     for e in range(G):
         if sizes[e]:
             r = slice(int(offs[e]), int(offs[e + 1]))
-            ref[r] = O.expert_ffn(x64[r], "swiglu", wg[e].double().numpy(), wu[e].double().numpy(),
+            ref[r] = O.expert_ffn(x64[r], act, wg[e].double().numpy(), wu[e].double().numpy(),
                                   wd[e].double().numpy())
     got = y.cpu().numpy().astype(np.float64)
     assert np.isfinite(got).all()
