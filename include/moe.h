@@ -94,6 +94,19 @@ typedef enum { MOE_OVERFLOW_DROP = 0, MOE_OVERFLOW_REROUTE = 1 } moe_overflow_t;
  *                      the linear layout's. */
 typedef enum { MOE_LAYOUT_LINEAR = 0, MOE_LAYOUT_PACKED = 1 } moe_layout_t;
 
+/* Explicit tile shape of the bf16 grouped expert GEMM (host struct; for tuning and tests).
+ *   rows   rows per M-tile: 32, 64, 128, 192 or 256; 0 = chosen from the sizes (the
+ *          expected rows per routed expert: capacity if set, else 1.6x the mean load)
+ *   waves  waves per workgroup: 4, 8 or 16; 0 = 8
+ * 192-row tiles exist with 8 waves only; with another explicit wave count and rows = 0
+ * the automatic height is raised from 192 to 256.  Any other value, or 192 rows with an
+ * explicit 4 or 16 waves, is MOE_EUNSUPPORTED.  The tile shape changes the schedule of the
+ * work, never a result bit.  fp32 layers have one tile shape and ignore it. */
+typedef struct moe_tile {
+  int32_t rows;
+  int32_t waves;
+} moe_tile_t;
+
 /* Static description of a status code (host). */
 const char* moe_status_string(moe_status_t s);
 /* Message of the last failing call on this host thread ("" if none). */
@@ -143,7 +156,9 @@ size_t moe_dispatch_workspace_bytes(int64_t T, int32_t E, int32_t k);
  * moe_dispatch - per-expert counts, capacity, expert-sorted permutation.
  *   [rkmt] §2.3: expert e accepts at most `capacity` slots; the overflow is dropped
  *   (zero contribution) or re-routed, see moe_priority_t and moe_overflow_t.
- *   topk_idx  [T, k] int32 in  (values in [0, E); other values are undefined behaviour)
+ *   topk_idx  [T, k] int32 in  (values in [0, E); other values are undefined behaviour).
+ *             A row may name one expert in several slots: each such slot is its own
+ *             row of that expert (in priority order), as any other slot.
  *   logits    [T, E] fp32 in  (the router logits; read only for MOE_OVERFLOW_REROUTE with
  *             capacity > 0, may be NULL otherwise)
  *   capacity  <= 0: unlimited
@@ -180,9 +195,10 @@ moe_status_t moe_dispatch(const int32_t* topk_idx, const float* logits, int64_t 
 moe_status_t moe_pack_weights(const void* w, void* packed, int64_t G, int64_t N, int64_t K,
                               hipStream_t stream);
 
-/* Workspace bytes moe_expert_ffn needs (host, pure). */
+/* Workspace bytes moe_expert_ffn needs (host, pure; tile as for moe_expert_ffn, may be
+ * NULL; 0 for an invalid size or tile). */
 size_t moe_expert_ffn_workspace_bytes(int64_t max_rows, int32_t G, int64_t d, int64_t F,
-                                      moe_act_t act, moe_dtype_t dt);
+                                      moe_act_t act, moe_dtype_t dt, const moe_tile_t* tile);
 
 /*
  * moe_expert_ffn - every group's FFN over its rows (grouped GEMM).
@@ -197,13 +213,16 @@ size_t moe_expert_ffn_workspace_bytes(int64_t max_rows, int32_t G, int64_t d, in
  *   max_rows host upper bound of offsets[G] (sizes the launch and the workspace)
  *   layout   moe_layout_t of w_gate, w_up and w_down (MOE_LAYOUT_PACKED: bf16 only)
  *   y        [max_rows, d] fp32 out: y[r] for r < min(offsets[G], max_rows)
- *   ws       device workspace of moe_expert_ffn_workspace_bytes(...) bytes
+ *   tile     host pointer to an explicit tile shape (moe_tile_t), or NULL for the
+ *            automatic choice
+ *   ws       device workspace of moe_expert_ffn_workspace_bytes(..., tile) bytes
  */
 moe_status_t moe_expert_ffn(const void* x, const int32_t* perm, int32_t k,
                             const int32_t* offsets, int32_t G, int64_t max_rows,
                             int64_t d, int64_t F, moe_act_t act, moe_dtype_t dt,
                             moe_layout_t layout, const void* w_gate, const void* w_up, const void* w_down,
-                            float* y, void* ws, size_t ws_bytes, hipStream_t stream);
+                            float* y, const moe_tile_t* tile, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
 
 /*
  * moe_combine - routing-weighted sum of the selected experts' outputs.
@@ -289,12 +308,24 @@ typedef struct moe_layer_args {
      NULL, or MOE_STATS_FLOATS(E) floats, with the three coefficients below. */
   float* stats;
   float lambda_balance, lambda_aux, gamma_aux;
+  /* Explicit tile shape of the expert FFN (moe_tile_t); all zero = automatic. */
+  moe_tile_t tile;
 } moe_layer_args_t;
 
 #define MOE_STAGE_EVENTS 7
 
 /* Workspace bytes moe_layer_forward needs for these arguments (host, pure). */
 size_t moe_layer_workspace_bytes(const moe_layer_args_t* a);
+
+/* How moe_layer_forward will run the expert FFN for these arguments (host, pure). */
+typedef struct moe_ffn_plan {
+  int32_t tile_rows;     /* rows per M-tile of the grouped GEMMs (fp32 layers: 64) */
+  int32_t tile_waves;    /* waves per workgroup (fp32 layers: 4) */
+  int32_t down_splits;   /* the down projection's contraction is split this many ways */
+} moe_ffn_plan_t;
+/* Fills *plan; MOE_EINVAL / MOE_EUNSUPPORTED for arguments the forward would reject on
+ * their sizes, enums or tile (pointers are not examined). */
+moe_status_t moe_layer_plan(const moe_layer_args_t* a, moe_ffn_plan_t* plan);
 
 /*
  * moe_layer_forward - the whole layer on one stream:

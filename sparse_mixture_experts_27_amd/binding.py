@@ -30,13 +30,22 @@ EXPORTS = ("moe_status_string", "moe_last_error", "moe_route_workspace_bytes", "
            "moe_capacity", "moe_dispatch_workspace_bytes",
            "moe_dispatch", "moe_pack_weights", "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine",
            "moe_routing_stats_workspace_bytes", "moe_routing_stats",
-           "moe_layer_workspace_bytes", "moe_layer_forward")
+           "moe_layer_workspace_bytes", "moe_layer_plan", "moe_layer_forward")
 
 
 class MoEError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"{STATUS.get(status, status)}: {msg}")
         self.status = status
+
+
+class Tile(C.Structure):
+    """moe_tile_t: explicit rows per M-tile and waves per workgroup (0 = automatic)."""
+    _fields_ = [("rows", C.c_int32), ("waves", C.c_int32)]
+
+
+class FfnPlan(C.Structure):
+    _fields_ = [("tile_rows", C.c_int32), ("tile_waves", C.c_int32), ("down_splits", C.c_int32)]
 
 
 class LayerArgs(C.Structure):
@@ -54,7 +63,7 @@ class LayerArgs(C.Structure):
                 ("ws", C.c_void_p), ("ws_bytes", C.c_size_t),
                 ("stage_events", C.POINTER(C.c_void_p)),
                 ("stats", C.c_void_p), ("lambda_balance", C.c_float), ("lambda_aux", C.c_float),
-                ("gamma_aux", C.c_float)]
+                ("gamma_aux", C.c_float), ("tile", Tile)]
 
 STAT_NAMES = ("balance_ratio", "l_balance", "l_aux", "entropy", "drop_rate")
 
@@ -92,10 +101,10 @@ def lib():
         L.moe_pack_weights.restype = C.c_int
         L.moe_pack_weights.argtypes = [vp, vp, i64, i64, i64, vp]
         L.moe_expert_ffn_workspace_bytes.restype = sz
-        L.moe_expert_ffn_workspace_bytes.argtypes = [i64, i32, i64, i64, C.c_int, C.c_int]
+        L.moe_expert_ffn_workspace_bytes.argtypes = [i64, i32, i64, i64, C.c_int, C.c_int, C.POINTER(Tile)]
         L.moe_expert_ffn.restype = C.c_int
         L.moe_expert_ffn.argtypes = [vp, vp, i32, vp, i32, i64, i64, i64, C.c_int, C.c_int, C.c_int,
-                                     vp, vp, vp, vp, vp, sz, vp]
+                                     vp, vp, vp, vp, C.POINTER(Tile), vp, sz, vp]
         L.moe_combine.restype = C.c_int
         L.moe_combine.argtypes = [vp, i64, vp, vp, vp, i64, i64, i32, C.c_int, vp, vp]
         L.moe_routing_stats_workspace_bytes.restype = sz
@@ -104,6 +113,8 @@ def lib():
         L.moe_routing_stats.argtypes = [vp, vp, vp, i64, i32, i32, C.c_float, C.c_float, C.c_float, vp, vp, sz, vp]
         L.moe_layer_workspace_bytes.restype = sz
         L.moe_layer_workspace_bytes.argtypes = [C.POINTER(LayerArgs)]
+        L.moe_layer_plan.restype = C.c_int
+        L.moe_layer_plan.argtypes = [C.POINTER(LayerArgs), C.POINTER(FfnPlan)]
         L.moe_layer_forward.restype = C.c_int
         L.moe_layer_forward.argtypes = [C.POINTER(LayerArgs), vp]
         _lib = L
@@ -211,9 +222,17 @@ def pack_weights(w):
     return out
 
 
-def expert_ffn(x, offsets, w_gate, w_up, w_down, max_rows, perm=None, k=1, act="swiglu", packed=False):
+def _tile(tile) -> Optional[Tile]:
+    """(rows, waves) -> moe_tile_t, None -> automatic."""
+    if tile is None:
+        return None
+    return Tile(int(tile[0]), int(tile[1]))
+
+
+def expert_ffn(x, offsets, w_gate, w_up, w_down, max_rows, perm=None, k=1, act="swiglu", packed=False,
+               tile=None):
     """-> y f32 [max_rows, d] (rows past offsets[G] unspecified).  packed: the weights were
-    reordered by pack_weights."""
+    reordered by pack_weights.  tile: (rows per M-tile, waves) or None (automatic)."""
     G = w_gate.shape[0]
     F, d = w_gate.shape[1], w_gate.shape[2]
     dev = x.device
@@ -223,10 +242,12 @@ def expert_ffn(x, offsets, w_gate, w_up, w_down, max_rows, perm=None, k=1, act="
     _req(perm, "perm", torch.int32, dev)
     a = MOE_ACT_SWIGLU if act == "swiglu" else MOE_ACT_GELU
     y = torch.empty((max(max_rows, 1), d), dtype=torch.float32, device=dev)
-    ws = _ws(lib().moe_expert_ffn_workspace_bytes(max_rows, G, d, F, a, _dt(x)), dev)
+    t = _tile(tile)
+    tp = None if t is None else C.byref(t)
+    ws = _ws(lib().moe_expert_ffn_workspace_bytes(max_rows, G, d, F, a, _dt(x), tp), dev)
     _check(lib().moe_expert_ffn(_ptr(x), _ptr(perm), k, _ptr(offsets), G, max_rows, d, F, a, _dt(x),
-                                MOE_LAYOUT_PACKED if packed else MOE_LAYOUT_LINEAR, _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(y), _ptr(ws), ws.numel(),
-                                _stream(dev)))
+                                MOE_LAYOUT_PACKED if packed else MOE_LAYOUT_LINEAR, _ptr(w_gate), _ptr(w_up),
+                                _ptr(w_down), _ptr(y), tp, _ptr(ws), ws.numel(), _stream(dev)))
     return y[:max_rows]
 
 
@@ -270,13 +291,14 @@ class Layer:
     prepacked=True: the expert weights given are already packed (pack_weights).
     capacity_factor: if given, the capacity of each call is capacity_rule(T, k, E,
     capacity_factor, min_capacity) for its T tokens (instead of the fixed `capacity`).
+    tile: (rows per M-tile, waves) of the expert FFN, or None for the automatic choice.
     """
 
     def __init__(self, w_r, w_gate, w_up, w_down, k, act="swiglu", bias=None, capacity=0,
                  s_gate=None, s_up=None, s_down=None, out_dtype=torch.float32, stats=False,
                  lambda_balance=0.01, lambda_aux=0.01, gamma_aux=100.0, weights="renormalized",
                  priority="token", overflow="drop", packed=False, prepacked=False, capacity_factor=None,
-                 min_capacity=0):
+                 min_capacity=0, tile=None):
         self.w_r, self.bias = w_r, bias
         self.w_gate, self.w_up, self.w_down = w_gate, w_up, w_down
         self.s_gate, self.s_up, self.s_down = s_gate, s_up, s_down
@@ -290,6 +312,7 @@ class Layer:
         self.priority = PRIORITIES[priority]
         self.overflow = OVERFLOWS[overflow]
         self.stat_coeffs = (lambda_balance, lambda_aux, gamma_aux)
+        self.tile = (0, 0) if tile is None else (int(tile[0]), int(tile[1]))
         self.act = MOE_ACT_SWIGLU if act == "swiglu" else MOE_ACT_GELU
         self.E = w_r.shape[1]
         self.F, self.d = w_gate.shape[1], w_gate.shape[2]
@@ -323,7 +346,22 @@ class Layer:
         if self.want_stats:
             a.stats = _ptr(self.stats)
             a.lambda_balance, a.lambda_aux, a.gamma_aux = self.stat_coeffs
+        a.tile = Tile(*self.tile)
         return a
+
+    def plan(self, T: int) -> dict:
+        """The expert-FFN plan moe_layer_forward uses for T tokens (moe_layer_plan)."""
+        a = LayerArgs()
+        a.dt = _dt(self.w_r)
+        a.act = self.act
+        a.T, a.d, a.F, a.E, a.k = T, self.d, self.F, self.E, self.k
+        a.capacity = (self.capacity if self.capacity_factor is None else
+                      capacity_rule(T, self.k, self.E, self.capacity_factor, self.min_capacity))
+        a.s_gate = _ptr(self.s_gate)
+        a.tile = Tile(*self.tile)
+        p = FfnPlan()
+        _check(lib().moe_layer_plan(C.byref(a), C.byref(p)))
+        return dict(tile_rows=p.tile_rows, tile_waves=p.tile_waves, down_splits=p.down_splits)
 
     def _buffers(self, x):
         T, dev, k = x.shape[0], x.device, self.k

@@ -91,6 +91,21 @@ moe_status_t check_bf16_operands(int64_t max_rows, int64_t d, int64_t F) {
   return MOE_OK;
 }
 
+// An explicit tile shape must name a kernel (moe_tile_t); NULL or zeros = automatic.
+moe_status_t check_tile(const moe_tile_t* t) {
+  if (!t) return MOE_OK;
+  const bool rows_ok = t->rows == 0 || t->rows == 32 || t->rows == 64 || t->rows == 128 || t->rows == 192 ||
+                       t->rows == 256;
+  const bool waves_ok = t->waves == 0 || t->waves == 4 || t->waves == 8 || t->waves == 16;
+  if (!rows_ok || !waves_ok || (t->rows == 192 && t->waves != 0 && t->waves != 8))
+    return fail(MOE_EUNSUPPORTED, "no expert FFN kernel for a tile of %d rows and %d waves "
+                "(rows 32/64/128/192/256, waves 4/8/16, 192 rows with 8 waves only; 0 = automatic)",
+                t->rows, t->waves);
+  return MOE_OK;
+}
+int tile_rows_of(const moe_tile_t* t) { return t ? t->rows : 0; }
+int tile_waves_of(const moe_tile_t* t) { return t ? t->waves : 0; }
+
 moe_status_t check_ffn_args(const void* x, const int32_t* offsets, int G, int64_t max_rows, int64_t d,
                             int64_t F, int act, int dt, const void* w_gate, const void* w_up,
                             const void* w_down, const void* y) {
@@ -191,9 +206,10 @@ moe_status_t moe_dispatch(const int32_t* topk_idx, const float* logits, int64_t 
 }
 
 size_t moe_expert_ffn_workspace_bytes(int64_t max_rows, int32_t G, int64_t d, int64_t F, moe_act_t act,
-                                      moe_dtype_t dt) {
+                                      moe_dtype_t dt, const moe_tile_t* tile) {
   if (max_rows < 0 || G < 1 || d < 1 || F < 1) return 0;
-  return ffn_plan(max_rows, G, 0, d, F, act, dt).ws_bytes;
+  if (check_tile(tile) != MOE_OK) return 0;
+  return ffn_plan(max_rows, G, 0, d, F, act, dt, 0, tile_rows_of(tile), tile_waves_of(tile)).ws_bytes;
 }
 
 moe_status_t moe_pack_weights(const void* w, void* packed, int64_t G, int64_t N, int64_t K, hipStream_t stream) {
@@ -215,12 +231,13 @@ moe_status_t moe_pack_weights(const void* w, void* packed, int64_t G, int64_t N,
 moe_status_t moe_expert_ffn(const void* x, const int32_t* perm, int32_t k, const int32_t* offsets, int32_t G,
                             int64_t max_rows, int64_t d, int64_t F, moe_act_t act, moe_dtype_t dt,
                             moe_layout_t layout, const void* w_gate, const void* w_up, const void* w_down, float* y,
-                            void* ws, size_t ws_bytes, hipStream_t stream) {
+                            const moe_tile_t* tile, void* ws, size_t ws_bytes, hipStream_t stream) {
   g_last_error[0] = 0;
   if (moe_status_t st = check_ffn_args(x, offsets, G, max_rows, d, F, act, dt, w_gate, w_up, w_down, y)) return st;
   if (moe_status_t st = check_layout(layout, dt)) return st;
+  if (moe_status_t st = check_tile(tile)) return st;
   if (perm && k < 1) return fail(MOE_EINVAL, "k must be >= 1 when perm is given");
-  const FfnPlan plan = ffn_plan(max_rows, G, 0, d, F, act, dt);
+  const FfnPlan plan = ffn_plan(max_rows, G, 0, d, F, act, dt, 0, tile_rows_of(tile), tile_waves_of(tile));
   if (!ws || ws_bytes < plan.ws_bytes)
     return fail(MOE_EWORKSPACE, "expert FFN needs %zu workspace bytes, got %zu", plan.ws_bytes, ws_bytes);
   FfnProblem p{};
@@ -261,7 +278,8 @@ static size_t layer_layout(const moe_layer_args_t* a, bool carve, WsCarver& c, i
   const int64_t T = a->T;
   const bool shared = a->s_gate != nullptr;
   const int64_t max_rows = T * a->k + (shared ? T : 0);
-  *plan = ffn_plan(max_rows, a->E, shared ? T : 0, a->d, a->F, a->act, a->dt, a->capacity);
+  *plan = ffn_plan(max_rows, a->E, shared ? T : 0, a->d, a->F, a->act, a->dt, a->capacity, a->tile.rows,
+                   a->tile.waves);
   float* lg = c.take<float>(static_cast<size_t>(T) * a->E);
   int32_t* ix = c.take<int32_t>(static_cast<size_t>(T) * a->k);
   float* tw = c.take<float>(static_cast<size_t>(T) * a->k);
@@ -295,6 +313,7 @@ static size_t layer_layout(const moe_layer_args_t* a, bool carve, WsCarver& c, i
 
 size_t moe_layer_workspace_bytes(const moe_layer_args_t* a) {
   if (!a || a->T < 0 || a->E < 1 || a->k < 1 || a->d < 1 || a->F < 1) return 0;
+  if (check_tile(&a->tile) != MOE_OK) return 0;
   WsCarver c(nullptr);
   int32_t *i, *cn, *of, *pm, *iv, *nd;
   float *w, *lg, *Y;
@@ -303,10 +322,45 @@ size_t moe_layer_workspace_bytes(const moe_layer_args_t* a) {
   return layer_layout(a, false, c, &i, &w, &lg, &cn, &of, &pm, &iv, &nd, &rws, &sws, &dws, &Y, &fws, &plan);
 }
 
+// Size, enum and tile checks of the layer arguments (no pointer is examined).
+static moe_status_t check_layer_sizes(const moe_layer_args_t* a) {
+  if (!valid_dt(a->dt)) return fail(MOE_EINVAL, "dtype %d is not MOE_F32 or MOE_BF16", a->dt);
+  if (a->T < 0 || a->T > (int64_t{1} << 31) - 1) return fail(MOE_EINVAL, "T=%lld out of range", (long long)a->T);
+  if (a->d < 1) return fail(MOE_EINVAL, "d=%lld must be >= 1", (long long)a->d);
+  if (a->E < 1 || a->E > kMaxExperts) return fail(MOE_EINVAL, "E=%d must be in [1, %d]", a->E, kMaxExperts);
+  if (a->k < 1 || a->k > a->E) return fail(MOE_EINVAL, "k=%d must be in [1, E=%d]", a->k, a->E);
+  if (a->T * a->k > (int64_t{1} << 31) - 1) return fail(MOE_EINVAL, "T*k exceeds 2^31-1");
+  if (route_lds_bytes(a->d, a->E, a->dt) > kMaxLdsBytes)
+    return fail(MOE_EUNSUPPORTED, "routing %d experts with d=%lld does not fit one workgroup's LDS", a->E,
+                (long long)a->d);
+  if (!valid_act(a->act)) return fail(MOE_EINVAL, "activation %d invalid", a->act);
+  if (a->F < 1) return fail(MOE_EINVAL, "F must be >= 1");
+  if (a->dt == MOE_BF16 && (a->d % 64 != 0 || a->F % 64 != 0))
+    return fail(MOE_EUNSUPPORTED, "bf16 layer needs d and F multiples of 64");
+  if (a->dt == MOE_BF16) {
+    if (moe_status_t st = check_bf16_operands(a->T * a->k + (a->s_gate ? a->T : 0), a->d, a->F)) return st;
+  }
+  return check_tile(&a->tile);
+}
+
+moe_status_t moe_layer_plan(const moe_layer_args_t* a, moe_ffn_plan_t* plan) {
+  g_last_error[0] = 0;
+  if (!a || !plan) return fail(MOE_EINVAL, "moe_layer_plan: null pointer");
+  if (moe_status_t st = check_layer_sizes(a)) return st;
+  const bool shared = a->s_gate != nullptr;
+  const FfnPlan pl = ffn_plan(a->T * a->k + (shared ? a->T : 0), a->E, shared ? a->T : 0, a->d, a->F, a->act,
+                              a->dt, a->capacity, a->tile.rows, a->tile.waves);
+  plan->tile_rows = pl.bm;
+  plan->tile_waves = a->dt == MOE_BF16 ? pl.nw : 4;
+  plan->down_splits = pl.splits;
+  return MOE_OK;
+}
+
 moe_status_t moe_layer_forward(const moe_layer_args_t* a, hipStream_t stream) {
   g_last_error[0] = 0;
   if (!a) return fail(MOE_EINVAL, "null args");
   if (moe_status_t st = check_route_args(a->x, a->w_r, a->dt, a->T, a->d, a->E, a->k, a->x, a->x, a->x)) return st;
+  if (moe_status_t st = check_tile(&a->tile)) return st;
   if (!valid_act(a->act)) return fail(MOE_EINVAL, "activation %d invalid", a->act);
   if (!valid_dt(a->out_dt)) return fail(MOE_EINVAL, "out dtype %d invalid", a->out_dt);
   if (a->weights != MOE_WEIGHTS_RENORMALIZED && a->weights != MOE_WEIGHTS_SOFTMAX)

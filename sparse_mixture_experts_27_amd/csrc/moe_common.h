@@ -84,9 +84,13 @@ struct FfnPlan {
   size_t ws_bytes;
 };
 // shared_rows: rows of the shared group inside max_rows (0 = none); capacity: per-group
-// row limit if known (0 = unknown).  Both only tune the tile height.
+// row limit if known (0 = unknown).  Both only tune the tile height.  tile_rows /
+// tile_waves: the caller's explicit tile shape (0 = the plan's own choice); a given shape
+// must pass bf16_tile_supported.
 FfnPlan ffn_plan(int64_t max_rows, int G, int64_t shared_rows, int64_t d, int64_t F, int act, int dt,
-                 int64_t capacity = 0);
+                 int64_t capacity, int tile_rows, int tile_waves);
+// Whether the bf16 grouped GEMM has a kernel for bm rows per M-tile and nw waves.
+bool bf16_tile_supported(int bm, int nw);
 // y: [splits][max_rows][d] fp32 partial sums when plan.splits > 1 and reduce_splits is
 // false; otherwise [max_rows][d] final.
 // ev (nullable): events recorded after the schedule, up-projection and down-projection.

@@ -129,8 +129,10 @@ __device__ void scatter_block(const int32_t* __restrict__ idx, SlotMap m, int E,
     }
   };
   // rank of slot j inside its expert e among this wave's slots: the lanes below me
-  // (earlier virtual tokens) that selected e in any of their slots (a token never
-  // selects one expert twice).  Up to KMAX slots per virtual token, each lane's choices
+  // (earlier virtual tokens) that selected e in any of their slots, plus this token's
+  // own earlier slots that selected e (a router never lists one expert twice, but a
+  // caller's topk_idx may; the slots then take distinct rows in slot order, as the
+  // token-major priority order (t, j) says).  Up to KMAX slots per virtual token, each lane's choices
   // stay in registers and every (slot, source lane) value is shuffled once for all of
   // this lane's slots: k*64 lane reads instead of k*k*64 (instantiated for 1, 2, 4 and 8
   // slots; more take the plain loop).  The source lane is a loop counter, the same in
@@ -154,6 +156,10 @@ __device__ void scatter_block(const int32_t* __restrict__ idx, SlotMap m, int E,
       }
     }
 #pragma unroll
+    for (int j = 1; j < KMAX; ++j)
+#pragma unroll
+      for (int j2 = 0; j2 < j; ++j2) rank[j] += (e[j2] == e[j]) ? 1 : 0;
+#pragma unroll
     for (int j = 0; j < KMAX; ++j)
       if (j < kv) place(j, e[j], rank[j]);
   };
@@ -171,6 +177,7 @@ __device__ void scatter_block(const int32_t* __restrict__ idx, SlotMap m, int E,
         const int32_t es = __builtin_amdgcn_readlane(v, src);
         rank += (src < lane && es == e) ? 1 : 0;
       }
+      rank += (j2 < j && e >= 0 && v == e) ? 1 : 0;     // this token's earlier slots
     }
     place(j, e, rank);
   }

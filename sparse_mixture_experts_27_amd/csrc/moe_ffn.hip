@@ -23,8 +23,6 @@
 // share its activation rows in that XCD's L2.
 #include "moe_common.h"
 
-#include <cstdlib>
-
 namespace moe {
 namespace {
 
@@ -411,6 +409,9 @@ __device__ __forceinline__ void ffn_gemm_bf16_body(const GemmArgs& p, uint16_t* 
     if (spread) {
 #pragma unroll
       for (int i = 0; i < AR; ++i) load_one(i, sta, lslot_n, stb, bslot_n);
+      // store_a's explicit wait counts on this phase's activation loads being issued
+      // before its weight loads: keep the scheduler from moving anything across
+      __builtin_amdgcn_sched_barrier(0);
     }
     bf16x8 a[PREFETCH ? 2 : 1][GS];
     if (PREFETCH) {
@@ -493,6 +494,7 @@ __device__ __forceinline__ void ffn_gemm_bf16_body(const GemmArgs& p, uint16_t* 
 #pragma unroll
     for (int st = B0; st < 0; ++st) {
       if (st + D >= 0) load_a(st + D, pm(st + D, 2), pm(st + D, LRING));
+      __builtin_amdgcn_sched_barrier(0);      // activations before weights (store_a's wait)
       load_b(st + WRING - 1, pm(st + WRING - 1, WRING));
       if (st + 1 >= 0) store_a(pm(st + 1, 2), pm(st + 1, LRING));
       barrier();
@@ -667,13 +669,6 @@ __global__ __launch_bounds__(256) void ffn_reduce_splits_kernel(const float* __r
   }
 }
 
-// Tile shapes with a bf16 kernel: 32, 64, 128 or 256 rows with 4, 8 or 16 waves, and 192
-// rows with 8 waves (12 row fragments; at 4 or 16 waves that height would need the register
-// path for the activations or more registers than a wave has).
-bool bf16_tile_supported(int bm, int nw) {
-  if (nw != 4 && nw != 8 && nw != 16) return false;
-  return bm == 32 || bm == 64 || bm == 128 || bm == 256 || (bm == 192 && nw == 8);
-}
 
 // Launch one bf16 grouped GEMM with the M-tile (MT*16 rows) chosen by the plan (a shape
 // that bf16_tile_supported accepts; the schedule was built for the same height).
@@ -716,6 +711,14 @@ void launch_bf16_gemm(bool packed, int bm, int nw, int64_t grid, const GemmArgs&
 
 }  // namespace
 
+// Tile shapes with a bf16 kernel: 32, 64, 128 or 256 rows with 4, 8 or 16 waves, and 192
+// rows with 8 waves (12 row fragments; at 4 or 16 waves that height would need the register
+// path for the activations or more registers than a wave has).
+bool bf16_tile_supported(int bm, int nw) {
+  if (nw != 4 && nw != 8 && nw != 16) return false;
+  return bm == 32 || bm == 64 || bm == 128 || bm == 256 || (bm == 192 && nw == 8);
+}
+
 // M-tile height: the smallest of 32/64/128/192/256 rows that holds a typical routed group
 // in one tile, so each expert's weights stream once.  The rows per group are only known on
 // the device; the host estimate is the capacity when one is set, else 1.6x the mean load
@@ -727,7 +730,7 @@ void launch_bf16_gemm(bool packed, int bm, int nw, int64_t grid, const GemmArgs&
 // adjacent in the schedule and share its weights in L2, while routed experts are the
 // bulk of the weight bytes.
 FfnPlan ffn_plan(int64_t max_rows, int G, int64_t shared_rows, int64_t d, int64_t F, int act, int dt,
-                 int64_t capacity) {
+                 int64_t capacity, int tile_rows, int tile_waves) {
   FfnPlan pl{};
   (void)act;
   const bool has_shared = shared_rows > 0;
@@ -738,14 +741,10 @@ FfnPlan ffn_plan(int64_t max_rows, int G, int64_t shared_rows, int64_t d, int64_
     if (capacity > 0 && static_cast<double>(capacity) < est) est = static_cast<double>(capacity);
     pl.bm = est <= 32 ? 32 : est <= 64 ? 64 : est <= 128 ? 128 : est <= 224 ? 192 : BM;
     pl.nw = 8;
-    // tuning overrides of the waves per workgroup (4, 8 or 16) and the tile height (32, 64,
-    // 128, 192 or 256 rows); a height without a kernel at that wave count becomes 256
-    if (const char* o = getenv("MOE_TILE_WAVES")) pl.nw = atoi(o) == 4 ? 4 : atoi(o) == 16 ? 16 : 8;
-    if (const char* o = getenv("MOE_TILE_ROWS")) {
-      const int v = atoi(o);
-      if (v == 32 || v == 64 || v == 128 || v == 192 || v == 256) pl.bm = v;
-    }
-    if (!bf16_tile_supported(pl.bm, pl.nw)) pl.bm = BM;
+    // the caller's explicit tile shape (moe_tile_t), already checked against the kernels
+    if (tile_waves > 0) pl.nw = tile_waves;
+    if (tile_rows > 0) pl.bm = tile_rows;
+    if (!bf16_tile_supported(pl.bm, pl.nw)) pl.bm = BM;     // waves alone: 192 rows need 8
   } else {
     pl.bm = BM_F32;
   }

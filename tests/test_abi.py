@@ -129,15 +129,16 @@ def test_dispatch_validation(lib):
 
 
 def test_ffn_validation(lib):
-    need = lib.moe_expert_ffn_workspace_bytes(8192, 64, 4096, 14336, B.MOE_ACT_SWIGLU, B.MOE_BF16)
+    need = lib.moe_expert_ffn_workspace_bytes(8192, 64, 4096, 14336, B.MOE_ACT_SWIGLU, B.MOE_BF16, None)
     assert need >= 8192 * 14336 * 2                     # holds the bf16 hidden activation
+    # x, perm, k, offsets, G, max_rows, d, F, act, dt, layout, w_gate, w_up, w_down, y, tile, ws, ws_bytes, stream
     base = [16, 16, 2, 16, 64, 8192, 4096, 14336, B.MOE_ACT_SWIGLU, B.MOE_BF16, B.MOE_LAYOUT_LINEAR,
-            16, 16, 16, 16, 16, need, None]
+            16, 16, 16, 16, None, 16, need, None]
     odd = list(base); odd[6] = 4000                    # d % 64 != 0 for bf16
     assert lib.moe_expert_ffn(*odd) == 2
     no_up = list(base); no_up[12] = None
     assert lib.moe_expert_ffn(*no_up) == 1
-    small = list(base); small[16] = need - 1
+    small = list(base); small[17] = need - 1
     assert lib.moe_expert_ffn(*small) == 3
     bad_act = list(base); bad_act[8] = 5
     assert lib.moe_expert_ffn(*bad_act) == 1
@@ -145,13 +146,68 @@ def test_ffn_validation(lib):
     assert lib.moe_expert_ffn(*bad_layout) == 1
     assert b"layout" in lib.moe_last_error()
     f32_packed = list(base); f32_packed[9] = B.MOE_F32; f32_packed[10] = B.MOE_LAYOUT_PACKED
-    f32_packed[16] = lib.moe_expert_ffn_workspace_bytes(8192, 64, 4096, 14336, B.MOE_ACT_SWIGLU, B.MOE_F32)
+    f32_packed[17] = lib.moe_expert_ffn_workspace_bytes(8192, 64, 4096, 14336, B.MOE_ACT_SWIGLU, B.MOE_F32, None)
     assert lib.moe_expert_ffn(*f32_packed) == 1
     assert b"bf16" in lib.moe_last_error()
     huge = list(base); huge[5] = 80000               # H = 80000 x 14336 bf16 rows > 2 GiB
-    huge[16] = lib.moe_expert_ffn_workspace_bytes(80000, 64, 4096, 14336, B.MOE_ACT_SWIGLU, B.MOE_BF16)
+    huge[17] = lib.moe_expert_ffn_workspace_bytes(80000, 64, 4096, 14336, B.MOE_ACT_SWIGLU, B.MOE_BF16, None)
     assert lib.moe_expert_ffn(*huge) == 2
     assert b"2 GiB" in lib.moe_last_error()
+
+
+@pytest.mark.parametrize("rows,waves,ok", [(0, 0, True), (32, 16, True), (192, 8, True), (192, 0, True),
+                                           (256, 4, True), (0, 16, True), (192, 4, False), (192, 16, False),
+                                           (96, 8, False), (64, 2, False), (-32, 8, False)])
+def test_tile_validation(lib, rows, waves, ok):
+    """An explicit tile must name a kernel; a bad one is rejected before any launch, and the
+    workspace query then returns 0."""
+    t = B.Tile(rows, waves)
+    need = lib.moe_expert_ffn_workspace_bytes(300, 8, 256, 512, B.MOE_ACT_SWIGLU, B.MOE_BF16, C.byref(t))
+    assert (need > 0) == ok
+    st = lib.moe_expert_ffn(16, None, 1, 16, 8, 300, 256, 512, B.MOE_ACT_SWIGLU, B.MOE_BF16, B.MOE_LAYOUT_LINEAR,
+                            16, 16, 16, 16, C.byref(t), None, 0, None)
+    # a valid tile reaches the workspace check (no workspace given), an invalid one stops at the tile
+    assert st == (3 if ok else 2)
+    if not ok:
+        assert b"tile" in lib.moe_last_error()
+
+
+def _layer_args(T=4096, E=64, k=2, capacity=0, shared=False, dt=None):
+    a = B.LayerArgs()
+    a.dt = B.MOE_BF16 if dt is None else dt
+    a.act, a.T, a.d, a.F, a.E, a.k = B.MOE_ACT_SWIGLU, T, 4096, 14336, E, k
+    a.capacity = capacity
+    if shared:
+        a.s_gate = a.s_up = a.s_down = 256
+    return a
+
+
+def test_layer_plan(lib):
+    """moe_layer_plan reports the tile the forward will use: the height follows the
+    expected rows per routed expert (capacity when set), an explicit tile wins, and few
+    tiles split the down projection."""
+    def plan(a):
+        p = B.FfnPlan()
+        assert lib.moe_layer_plan(C.byref(a), C.byref(p)) == 0, lib.moe_last_error()
+        return p.tile_rows, p.tile_waves, p.down_splits
+    assert plan(_layer_args()) == (192, 8, 1)                       # 128 rows per expert on average
+    assert plan(_layer_args(T=8192, E=16, shared=True)) == (256, 8, 1)
+    assert plan(_layer_args(T=1024, E=16, capacity=128)) == (128, 8, 1)
+    assert plan(_layer_args(T=16)) == (32, 8, 1)
+    assert plan(_layer_args(T=1))[2] > 1                            # a couple of tiles: split over K
+    a = _layer_args()
+    a.tile = B.Tile(64, 4)
+    assert plan(a)[:2] == (64, 4)
+    a.tile = B.Tile(0, 16)                                          # 192 rows need 8 waves
+    assert plan(a)[:2] == (256, 16)
+    a.tile = B.Tile(192, 4)
+    p = B.FfnPlan()
+    assert lib.moe_layer_plan(C.byref(a), C.byref(p)) == 2
+    assert plan(_layer_args(T=64, dt=B.MOE_F32))[:2] == (64, 4)
+    bad = _layer_args()
+    bad.k = 65
+    assert lib.moe_layer_plan(C.byref(bad), C.byref(p)) == 1
+    assert lib.moe_layer_plan(None, C.byref(p)) == 1
 
 
 def test_pack_validation(lib):
