@@ -8,7 +8,9 @@ A step is one moe_layer_forward (route, dispatch, grouped expert FFN, combine).
 
 Prints ONE JSON line: tokens/s, the roofline of the dominant kernel (the gate/up grouped
 GEMM) measured with HIP events recorded by the library on its stream, and the CPU
-oracle timed on a bounded sample of the same workload.
+oracle timed on a bounded sample of the same workload.  The default run also measures
+the decode-shaped layer (T=16, same E, k, d, F) and reports it as the `decode` object:
+its tokens/s and the fraction of the HBM bandwidth its touched experts' weights reach.
 """
 from __future__ import annotations
 
@@ -35,7 +37,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2, help="workload number 1-7 (default 2: prefill, E=64)")
+    ap.add_argument("--config", type=int, default=2,
+                    help="workload number 1-8 (default 2: prefill, E=64; the decode workload, 5, is then "
+                         "measured in the same run and reported as the `decode` object)")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode workload of the default run")
     ap.add_argument("--priority", choices=("token", "slot"), default=None,
                     help="capacity priority (default: the workload's, token-major)")
     ap.add_argument("--overflow", choices=("drop", "reroute"), default=None,
@@ -101,21 +106,24 @@ def layer_counts(cfg, L):
 
 
 def algorithmic(cfg, touched, rows):
-    """Bytes and flops the method must touch (weights of touched experts once, x once,
-    outputs once), per stage and for the whole layer."""
+    """What the method must touch, per stage and for the whole layer: the weights of the
+    touched experts once, the hidden states x once, the output once (and W_r), and the
+    flops of the kept rows.  The hidden activation H (written by gate/up, read by down) and
+    the per-row expert outputs are implementation traffic: reported, not counted."""
     b = 2 if cfg.dtype == "bf16" else 4
     mats_up = 2 if cfg.act == "swiglu" else 1
     T, d, F, E = cfg.T, cfg.d, cfg.F, cfg.E
     sh_rows = T if cfg.shared else 0
     n_exp = touched + (1 if cfg.shared else 0)
-    up_bytes = n_exp * mats_up * F * d * b + T * d * b + (rows + sh_rows) * F * b
+    up_bytes = n_exp * mats_up * F * d * b + T * d * b
     up_flops = 2.0 * (rows + sh_rows) * F * d * mats_up
-    down_bytes = n_exp * d * F * b + (rows + sh_rows) * F * b + (rows + sh_rows) * d * 4
+    down_bytes = n_exp * d * F * b
     down_flops = 2.0 * (rows + sh_rows) * d * F
     layer_bytes = n_exp * (mats_up + 1) * F * d * b + T * d * b + d * E * b + T * d * b
     layer_flops = 2.0 * T * d * E + up_flops + down_flops
+    impl = dict(h_write=(rows + sh_rows) * F * b, h_read=(rows + sh_rows) * F * b, y_write=(rows + sh_rows) * d * 4)
     return dict(up_bytes=up_bytes, up_flops=up_flops, down_bytes=down_bytes, down_flops=down_flops,
-                layer_bytes=layer_bytes, layer_flops=layer_flops)
+                layer_bytes=layer_bytes, layer_flops=layer_flops, impl=impl)
 
 
 def roofline(bytes_, flops, seconds, dtype):
@@ -179,6 +187,104 @@ def cpu_baseline(cfg, inp, L, n_exp):
                 seconds=round(t_oracle, 2))
 
 
+def load_layer(cfg, packed):
+    """Seeded inputs of the workload on cuda:0 and its layer (expert weights packed once at
+    load time, one tensor at a time, each linear copy freed once its packed copy exists)."""
+    import torch
+    from sparse_mixture_experts_27_amd import binding as B
+    from sparse_mixture_experts_27_amd import synth
+    dev = torch.device("cuda", 0)
+    inp = synth.make_inputs(cfg, dev)
+    if packed:
+        for name in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down"):
+            if inp[name] is not None:
+                inp[name] = B.pack_weights(inp[name])
+                torch.cuda.synchronize()
+                torch.cuda.empty_cache()
+    L = B.Layer(inp["w_r"], inp["w_gate"], inp["w_up"], inp["w_down"], cfg.k, act=cfg.act, bias=inp["bias"],
+                capacity=cfg.capacity, s_gate=inp["s_gate"], s_up=inp["s_up"], s_down=inp["s_down"],
+                weights=cfg.weights, priority=cfg.priority, overflow=cfg.overflow, prepacked=packed)
+    return inp, L
+
+
+def time_layer(cfg, L, x, steps, warmup, graph):
+    """Warm-up, then `steps` forwards between two synchronisations -> (seconds, stage ms).
+    The library records its stage events on its stream in every timed eager step."""
+    import torch
+    from sparse_mixture_experts_27_amd import binding as B
+    for _ in range(warmup):
+        L(x)
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(steps):
+        row = [torch.cuda.Event(enable_timing=True) for _ in range(B.STAGE_EVENTS)]
+        for e in row:
+            e.record()                           # create the underlying HIP events
+        evs.append(row)
+    torch.cuda.synchronize()
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            L(x)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        for i in range(steps):                   # stage times: the same kernels, eager
+            L(x, stage_events=evs[i])
+        torch.cuda.synchronize()
+    else:
+        t0 = time.perf_counter()
+        for i in range(steps):
+            L(x, stage_events=evs[i])
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    stage_ms = {name: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]))
+                for j, name in enumerate(B.STAGES)}
+    return elapsed, stage_ms
+
+
+def measure(cfg, args, packed, graph):
+    """One workload: tokens/s, the rooflines of its GEMMs and of the whole step, routing
+    facts, and (unless disabled) the oracle baseline."""
+    import torch
+    inp, L = load_layer(cfg, packed)
+    elapsed, stage_ms = time_layer(cfg, L, inp["x"], args.steps, args.warmup, graph)
+    ms_step = elapsed / args.steps * 1e3
+    kept, touched, rows = layer_counts(cfg, L)
+    alg = algorithmic(cfg, touched, rows)
+    up_s = stage_ms["ffn_up"] / 1e3
+    roof = roofline(alg["up_bytes"], alg["up_flops"], up_s, cfg.dtype)
+    roof["algorithmic_bytes"] = int(alg["up_bytes"])
+    roof["kernel"] = "ffn_gemm_bf16_kernel<SwiGLU up>" if cfg.dtype == "bf16" else "ffn_gemm_f32_kernel<up>"
+    peak_t = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    mfma_t = alg["up_flops"] / up_s / 1e12
+    out = dict(
+        value=round(cfg.T * args.steps / elapsed, 1),
+        ms_per_step=round(ms_step, 4),
+        roofline=roof,
+        mfma_utilization=dict(kernel=roof["kernel"], achieved=round(mfma_t, 1), peak=peak_t, unit="TFLOP/s",
+                              frac=round(mfma_t / peak_t, 4)),
+        layer_roofline=roofline(alg["layer_bytes"], alg["layer_flops"], ms_step / 1e3, cfg.dtype),
+        down_roofline=roofline(alg["down_bytes"], alg["down_flops"], stage_ms["ffn_down"] / 1e3, cfg.dtype),
+        implementation_bytes=alg["impl"],
+        stage_ms={k: round(v, 4) for k, v in stage_ms.items()},
+        plan=L.plan(cfg.T),
+        routing={"touched_experts": touched, "rows": rows, "load_min": int(kept.min()),
+                 "load_max": int(kept.max()), "n_dropped": int(L.n_dropped.item()),
+                 "drop_rate": round(int(L.n_dropped.item()) / (cfg.T * cfg.k), 4)},
+    )
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, L, args.cpu_experts)
+    del L, inp
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -190,87 +296,25 @@ def main():
         sys.exit(2)
     import torch
     from sparse_mixture_experts_27_amd import binding as B
-    from sparse_mixture_experts_27_amd import synth
     from sparse_mixture_experts_27_amd.configs import CONFIGS
 
     cfg = CONFIGS[args.config]
     if args.priority or args.overflow:
         cfg = cfg.scaled(priority=args.priority or cfg.priority, overflow=args.overflow or cfg.overflow)
     B.lib()                                  # fail loudly if the HIP library is missing
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-    inp = synth.make_inputs(cfg, dev)
+    torch.cuda.set_device(0)
     packed = args.layout == "packed" and cfg.dtype == "bf16"
-    if packed:
-        # one tensor at a time, each linear copy freed once its packed copy exists
-        for name in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down"):
-            if inp[name] is not None:
-                inp[name] = B.pack_weights(inp[name])
-                torch.cuda.synchronize()
-                torch.cuda.empty_cache()
-    L = B.Layer(inp["w_r"], inp["w_gate"], inp["w_up"], inp["w_down"], cfg.k, act=cfg.act, bias=inp["bias"],
-                capacity=cfg.capacity, s_gate=inp["s_gate"], s_up=inp["s_up"], s_down=inp["s_down"],
-                weights=cfg.weights, priority=cfg.priority, overflow=cfg.overflow, prepacked=packed)
-    x = inp["x"]
-    for _ in range(args.warmup):
-        L(x)
-    torch.cuda.synchronize()
-
-    evs = []
-    for _ in range(args.steps):
-        row = [torch.cuda.Event(enable_timing=True) for _ in range(B.STAGE_EVENTS)]
-        for e in row:
-            e.record()                           # create the underlying HIP events
-        evs.append(row)
-    torch.cuda.synchronize()
-
-    if args.graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            L(x)
-        graph.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            graph.replay()
-        torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
-        for i in range(args.steps):              # stage times: the same kernels, eager
-            L(x, stage_events=evs[i])
-        torch.cuda.synchronize()
-    else:
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            L(x, stage_events=evs[i])
-        torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
-
-    stage_ms = {name: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
-                for j, name in enumerate(B.STAGES)}
-    ms_step = elapsed / args.steps * 1e3
-    value = cfg.T * args.steps / elapsed
-    kept, touched, rows = layer_counts(cfg, L)
-    alg = algorithmic(cfg, touched, rows)
-    up_s = stage_ms["ffn_up"] / 1e3
-    roof = roofline(alg["up_bytes"], alg["up_flops"], up_s, cfg.dtype)
-    roof["traffic"] = measured_traffic(cfg.name, "packed" if packed else "linear")
-    roof["kernel"] = "ffn_gemm_bf16_kernel<SwiGLU up>" if cfg.dtype == "bf16" else "ffn_gemm_f32_kernel<up>"
-    layer_roof = roofline(alg["layer_bytes"], alg["layer_flops"], ms_step / 1e3, cfg.dtype)
-    # the metric also asks for the share of the MFMA peak, whichever roof binds
-    peak_t = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
-    mfma_t = alg["up_flops"] / up_s / 1e12
-    mfma = dict(kernel=roof.get("kernel", "gate/up GEMM"), achieved=round(mfma_t, 1), peak=peak_t,
-                unit="TFLOP/s", frac=round(mfma_t / peak_t, 4))
-    down_roof = roofline(alg["down_bytes"], alg["down_flops"], stage_ms["ffn_down"] / 1e3, cfg.dtype)
+    m = measure(cfg, args, packed, args.graph)
+    m["roofline"]["traffic"] = measured_traffic(cfg.name, "packed" if packed else "linear")
 
     line = {
         "metric": "MoE-layer tokens/s at E=64,k=2; % bf16 MFMA peak (prefill), % HBM BW (decode)",
-        "value": round(value, 1),
+        "value": m["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": m["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -281,16 +325,20 @@ def main():
                    "overflow": cfg.overflow, "weight_layout": "packed" if packed else "linear",
                    "launch": "hip graph replay" if args.graph else "eager",
                    "parallelism": "single-gpu"},
-        "roofline": roof,
-        "mfma_utilization": mfma,
-        "layer_roofline": layer_roof,
-        "down_roofline": down_roof,
-        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
-        "routing": {"touched_experts": touched, "rows": rows, "load_min": int(kept.min()),
-                    "load_max": int(kept.max()), "n_dropped": int(L.n_dropped.item())},
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, inp, L, args.cpu_experts)
+    line.update({k: v for k, v in m.items() if k not in ("value", "ms_per_step")})
+    # the metric's other half: the decode-shaped layer (E=64, k=2, T=16), measured in the
+    # same process on its own seeded weights, against the HBM roofline of the weights of
+    # the experts it touches
+    if args.config == 2 and not args.no_decode:
+        dcfg = CONFIGS[5]
+        dm = measure(dcfg, args, packed, args.graph)
+        line["decode"] = {"workload": dcfg.label, "value": dm["value"], "unit": "tokens/s",
+                          "ms_per_step": dm["ms_per_step"], "roofline": dm["layer_roofline"],
+                          "gate_up_roofline": dm["roofline"], "down_roofline": dm["down_roofline"],
+                          "stage_ms": dm["stage_ms"], "plan": dm["plan"], "routing": dm["routing"]}
+        if "cpu_baseline" in dm:
+            line["decode"]["cpu_baseline"] = dm["cpu_baseline"]
     print(json.dumps(line), flush=True)
 
 

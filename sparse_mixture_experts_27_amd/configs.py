@@ -56,6 +56,12 @@ CONFIGS = {
     6: MoEConfig("wide-e384-top6-shared", 6, T=4096, d=4096, E=384, k=6, F=14336, act="swiglu", dtype="bf16",
                  shared=True),
     7: MoEConfig("wide-e128-top2", 7, T=4096, d=4096, E=128, k=2, F=14336, act="swiglu", dtype="bf16"),
+    # the capacity-limited layer in the drop regime its description aims at (5-20% of the
+    # slots dropped): offsets drawn literally from N(0, 1) drop about 41% of the slots at
+    # C = 128 ([rkmt] §2.3 sets its alarm at a 5% drop rate), so this variant draws them
+    # with standard deviation 0.25 (variance 1/16), which drops 18.0% with its seed
+    8: MoEConfig("capacity-e16-calibrated", 8, T=1024, d=4096, E=16, k=2, F=14336, act="swiglu",
+                 dtype="bf16", capacity=128, bias_var=0.0625),
 }
 
 # the workloads by name

@@ -85,3 +85,39 @@ def to_numpy(t: Optional[torch.Tensor]) -> Optional[np.ndarray]:
     if t is None:
         return None
     return t.detach().to("cpu", torch.float64).numpy()
+
+
+def tie_router_inputs(T: int, d: int, E: int, seed: int, dtype=torch.bfloat16, offsets: bool = True):
+    """Router inputs whose logits tie exactly, on any summation order.
+
+    Every hidden state is one-hot (a single 1.0 in a random column r_t), so token t's
+    logit for expert e is the single product W_r[r_t, e] (plus the offset b[e]); all other
+    terms are exact zeros.  W_r entries are multiples of 1/4 drawn from 3 to 9 levels per
+    row, the offsets multiples of 1/4 in [-1/2, 1/2]: sums are exact in fp32, and with so
+    few levels many experts share the largest logits, so ties fall inside the top-k and
+    across the k-th / (k+1)-th boundary.  Some zero entries are negative zeros.
+    Returns (x [T, d], w_r [d, E], bias [E] fp32 or None) as CPU tensors of `dtype`."""
+    rng = np.random.default_rng(seed)
+    x = np.zeros((T, d), np.float32)
+    x[np.arange(T), rng.integers(0, d, size=T)] = 1.0
+    lev = rng.integers(1, 5, size=(d, 1))
+    w = (rng.integers(-4, 5, size=(d, E)) % (2 * lev + 1) - lev).astype(np.float32) / 4.0
+    w[(w == 0) & (rng.random((d, E)) < 0.5)] = -0.0
+    b = None
+    if offsets:
+        b = rng.integers(-2, 3, size=E).astype(np.float32) / 4.0
+        b[(b == 0) & (rng.random(E) < 0.5)] = -0.0
+        b = torch.from_numpy(b)
+    return torch.from_numpy(x).to(dtype), torch.from_numpy(w).to(dtype), b
+
+
+def tie_logits(T: int, E: int, seed: int, skew: float = 0.0) -> torch.Tensor:
+    """fp32 logits [T, E] with exact ties: integers in [-2, 2] (a quarter of the zeros
+    negative zeros), plus an optional per-expert integer skew rounded from
+    skew * (E - 1 - e) / E so that a few experts overflow their capacity."""
+    rng = np.random.default_rng(seed)
+    z = rng.integers(-2, 3, size=(T, E)).astype(np.float32)
+    if skew:
+        z += np.round(skew * (E - 1 - np.arange(E)) / E).astype(np.float32)[None, :]
+    z[(z == 0) & (rng.random((T, E)) < 0.25)] = -0.0
+    return torch.from_numpy(z)

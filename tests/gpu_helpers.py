@@ -1,11 +1,17 @@
 """Shared helpers of the GPU parity tests: run the HIP layer, compare with the oracle.
 
 Comparison rules (stage-wise and teacher-forced, so one near-tie flip cannot cascade):
-  * route: logits within 1e-4 relative (bf16 inputs; 1e-5 for fp32); the selected set
-    must equal the oracle's on every token whose k-th vs (k+1)-th oracle logit margin
-    exceeds 1e-4 (flips below it are counted and reported); slot order must match
-    wherever every gap inside the top-k exceeds 1e-4, else slots are compared as a set
-    keyed by expert; weights within 1e-5 absolute.
+  * route: logits within 1e-4 relative (bf16 inputs; 1e-5 for fp32).  The top-k stage
+    on the GPU's own fp32 logits is bit-exact on EVERY token, slot order included: the
+    GPU's selection equals the oracle's selection rule applied to the GPU's logits, so
+    an exact tie must go to the lowest index with no margin excuse; its weights match
+    the oracle's weights of those logits within 1e-5.  Against the oracle's own logits:
+    on every token whose fp32 logit row equals the oracle's bit for bit (-0 == +0) the
+    selection must be the oracle's, whatever its margin; elsewhere the selected set must
+    equal the oracle's where the k-th vs (k+1)-th oracle logit margin exceeds 1e-4 (flips
+    below it, which come from a different fp32 summation order, are counted and
+    reported); slot order must match wherever every gap inside the top-k exceeds 1e-4;
+    weights within 1e-5 absolute of the oracle's weights of the GPU's selection.
   * dispatch: the oracle's dispatch of the GPU's own selection, bit-exact.
   * expert FFN + combine: the oracle's FFN and combine on the GPU's selection and the
     oracle's weights for it; max |out - ref| <= tol * RMS(ref) with tol = 1e-4 (fp32
@@ -37,11 +43,11 @@ def say(msg: str):
     sys.stdout.flush()
 
 
-def layer_for(cfg, inp, out_dtype=torch.float32, packed=False):
+def layer_for(cfg, inp, out_dtype=torch.float32, packed=False, tile=None):
     return B.Layer(inp["w_r"], inp["w_gate"], inp["w_up"], inp["w_down"], cfg.k, act=cfg.act,
                    bias=inp["bias"], capacity=cfg.capacity, s_gate=inp["s_gate"], s_up=inp["s_up"],
                    s_down=inp["s_down"], out_dtype=out_dtype, weights=cfg.weights, priority=cfg.priority,
-                   overflow=cfg.overflow, packed=packed)
+                   overflow=cfg.overflow, packed=packed, tile=tile)
 
 
 def half_ulp_bf16(v: np.ndarray) -> np.ndarray:
@@ -50,8 +56,8 @@ def half_ulp_bf16(v: np.ndarray) -> np.ndarray:
     return np.where(v == 0, 0.0, np.ldexp(1.0, ex - 9))
 
 
-def run_layer(cfg, inp, out_dtype=torch.float32, packed=False) -> Dict[str, np.ndarray]:
-    L = layer_for(cfg, inp, out_dtype, packed)
+def run_layer(cfg, inp, out_dtype=torch.float32, packed=False, tile=None) -> Dict[str, np.ndarray]:
+    L = layer_for(cfg, inp, out_dtype, packed, tile)
     out = L(inp["x"])
     torch.cuda.synchronize()
     res = dict(out=out.float().cpu().numpy().astype(np.float64),
@@ -92,11 +98,22 @@ def check_route(cfg, x64, w_r64, bias64, res, report: dict):
     rel = np.abs(z_g.astype(np.float64) - z_o) / (1.0 + np.abs(z_o))
     ztol = 1e-5 if cfg.dtype == "f32" else 1e-4
     assert rel.max() <= ztol, f"logits differ: max rel {rel.max():.3g}"
+    # the top-k stage, teacher-forced on the GPU's own logits: bit-exact on every token
+    idx_gz = O.select_topk(z_g.astype(np.float64), cfg.k)
+    bad = np.any(res["idx"] != idx_gz, axis=1)
+    assert not bad.any(), (f"top-k of the GPU's own logits differs on {int(bad.sum())} tokens "
+                           f"(first {int(np.argmax(bad))}: {res['idx'][bad][0].tolist()} vs {idx_gz[bad][0].tolist()})")
+    w_gz = O.topk_weights(z_g.astype(np.float64), res["idx"], cfg.weights)
+    assert np.abs(res["w"] - w_gz).max(initial=0.0) <= 1e-5, "weights of the GPU's own logits differ"
     idx_o = O.select_topk(z_o, cfg.k)
     margin = O.topk_margin(z_o, cfg.k)
     set_g = np.sort(res["idx"], axis=1)
     set_o = np.sort(idx_o, axis=1)
     flip = np.any(set_g != set_o, axis=1)
+    same_row = np.all(z_g == z_o, axis=1)
+    assert not np.any(flip & same_row), \
+        f"selection differs on {int(np.sum(flip & same_row))} tokens whose logits equal the oracle's"
+    assert np.array_equal(res["idx"][same_row], idx_o[same_row]), "slot order differs on exact-logit tokens"
     assert not np.any(flip & (margin > MARGIN)), \
         f"selection differs on {int(np.sum(flip & (margin > MARGIN)))} tokens with margin > {MARGIN}"
     # slot order where the top-k gaps are all clear
@@ -107,7 +124,8 @@ def check_route(cfg, x64, w_r64, bias64, res, report: dict):
     w_o = O.topk_weights(z_o, res["idx"], cfg.weights)
     assert np.abs(res["w"] - w_o)[~flip].max(initial=0.0) <= 1e-5, "routing weights differ"
     report.update(route_flips=int(flip.sum()), min_margin=float(margin.min()),
-                  max_logit_rel=float(rel.max()))
+                  max_logit_rel=float(rel.max()), exact_logit_tokens=int(same_row.sum()),
+                  exact_ties=int(np.sum(margin == 0)))
     return z_o, flip
 
 

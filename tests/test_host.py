@@ -58,14 +58,17 @@ def test_input_recipe_statistics():
 
 
 def test_workload_table():
-    """The seven workloads and their shapes (the benchmark measures number 2)."""
-    assert len(CONFIGS) == 7
+    """The eight workloads and their shapes (the benchmark measures number 2, and number 5
+    beside it)."""
+    assert len(CONFIGS) == 8
     p = BY_NAME["prefill-e64"]
     assert (p.T, p.d, p.E, p.k, p.F, p.act, p.dtype) == (4096, 4096, 64, 2, 14336, "swiglu", "bf16")
     assert CONFIGS[2] is p
     assert BY_NAME["capacity-e16"].capacity == 128           # (1024 x 2) / 16
     assert BY_NAME["shared-routed-e16"].shared and BY_NAME["wide-e384-top6-shared"].shared
     assert BY_NAME["decode-e64"].T == 16
+    cal = BY_NAME["capacity-e16-calibrated"]
+    assert (cal.T, cal.E, cal.k, cal.capacity) == (1024, 16, 2, 128) and cal.bias_var == 0.25 ** 2
 
 
 def test_bench_rejects_several_gpus():
@@ -85,7 +88,8 @@ def test_bench_traffic_record_matches_the_sources():
     with open(bench.TRAFFIC_FILE) as f:
         t = json.load(f)
     assert t["workload"] == "prefill-e64" and t["weight_layout"] == "packed"
-    assert bench.measured_traffic("prefill-e64", "packed") == t["hbm_bytes_per_launch"]
+    fresh = t["ffn_source_sha256_16"] == bench.source_digest(bench.FFN_SOURCE)
+    assert bench.measured_traffic("prefill-e64", "packed") == (t["hbm_bytes_per_launch"] if fresh else None)
     assert bench.measured_traffic("prefill-e64", "linear") is None
     alg = t["algorithmic_bytes_per_launch"]
     assert 1.0 <= t["hbm_bytes_per_launch"] / alg < 1.05

@@ -64,9 +64,9 @@ def _x64(inp):
     return synth.to_numpy(inp["x"]), synth.to_numpy(inp["w_r"]), synth.to_numpy(inp["bias"])
 
 
-def _run_and_check(cfg, inp, tokens=None, out_dtype=torch.float32, packed=False):
-    say(f"[case] {cfg.label} out={out_dtype} packed={packed}")
-    res = run_layer(cfg, inp, out_dtype, packed)
+def _run_and_check(cfg, inp, tokens=None, out_dtype=torch.float32, packed=False, tile=None):
+    say(f"[case] {cfg.label} out={out_dtype} packed={packed} tile={tile}")
+    res = run_layer(cfg, inp, out_dtype, packed, tile=tile)
     x64, wr64, b64 = _x64(inp)
     report = {}
     z_o, flip = check_route(cfg, x64, wr64, b64, res, report)
@@ -274,55 +274,45 @@ def test_pack_weights_layout(G, N, K):
         assert np.array_equal(p2.cpu().view(torch.int16).numpy(), got[0])
 
 
-# tile height (MOE_TILE_ROWS) and waves per workgroup (MOE_TILE_WAVES); None = the plan's own
-# choice; 192 rows with 4 waves has no kernel and runs as 256 rows
-TILES = [None, ("256", "16"), ("192", "8"), ("192", "4"), ("128", "4"), ("64", "8"), ("32", "16")]
+# explicit tiles (rows per M-tile, waves per workgroup); None = the plan's own choice;
+# (0, 4) = the automatic height with 4 waves (192 rows have no 4-wave kernel: 256 rows)
+TILES = [None, (256, 16), (192, 8), (0, 4), (128, 4), (64, 8), (32, 16)]
 
 
 @pytest.mark.parametrize("name", ["bf16-swiglu-multitile", "bf16-gelu", "bf16-shared-bias", "bf16-decode",
                                   "bf16-capacity-reroute", "bf16-e384-top6-shared"])
-def test_packed_weights_bit_identical(name, monkeypatch):
+def test_packed_weights_bit_identical(name):
     """The packed layout feeds the MFMAs the same operands in the same order: every tile
     shape gives the same bits as the linear layout under that shape."""
     cfg = SMALL[name]
     inp = synth.make_inputs(cfg, DEV)
     for tile in TILES:
-        if tile is None:
-            monkeypatch.delenv("MOE_TILE_ROWS", raising=False)
-            monkeypatch.delenv("MOE_TILE_WAVES", raising=False)
-        else:
-            monkeypatch.setenv("MOE_TILE_ROWS", tile[0])
-            monkeypatch.setenv("MOE_TILE_WAVES", tile[1])
         say(f"[case] packed vs linear {cfg.label} tile={tile}")
-        lin = layer_for(cfg, inp)(inp["x"]).clone()
-        pk = layer_for(cfg, inp, packed=True)(inp["x"]).clone()
+        lin = layer_for(cfg, inp, tile=tile)(inp["x"]).clone()
+        pk = layer_for(cfg, inp, packed=True, tile=tile)(inp["x"]).clone()
         torch.cuda.synchronize()
         assert torch.equal(lin.view(torch.int32), pk.view(torch.int32)), tile
 
 
 @pytest.mark.parametrize("tile", TILES[1:])
-def test_tile_overrides_against_oracle(tile, monkeypatch):
-    """Every tile shape the tuning overrides can select, packed, against the oracle."""
-    monkeypatch.setenv("MOE_TILE_ROWS", tile[0])
-    monkeypatch.setenv("MOE_TILE_WAVES", tile[1])
+def test_tile_overrides_against_oracle(tile):
+    """Every explicit tile shape, packed, against the oracle."""
     cfg = SMALL["bf16-shared-bias"]
-    _run_and_check(cfg, synth.make_inputs(cfg, DEV), packed=True)
+    _run_and_check(cfg, synth.make_inputs(cfg, DEV), packed=True, tile=tile)
 
 
 # group sizes on both sides of a tile height (and of two tiles), a one-row group and an
 # empty group, for every tile shape the plan can pick
-EDGE_TILES = [("32", "8"), ("64", "8"), ("128", "8"), ("192", "8"), ("256", "8"), ("256", "16"), ("128", "4")]
+EDGE_TILES = [(32, 8), (64, 8), (128, 8), (192, 8), (256, 8), (256, 16), (128, 4)]
 
 
 @pytest.mark.parametrize("act", ["swiglu", "gelu"])
 @pytest.mark.parametrize("tile", EDGE_TILES, ids=[f"{t[0]}x{t[1]}" for t in EDGE_TILES])
-def test_group_sizes_around_tile_heights(tile, act, monkeypatch):
+def test_group_sizes_around_tile_heights(tile, act):
     """moe_expert_ffn on identity rows with groups of h-1, h, h+1, 1, 0 and 2h+3 rows for
     tile height h: every row against the oracle's FFN of its group, packed weights bit
     for bit equal to the nn.Linear layout."""
-    monkeypatch.setenv("MOE_TILE_ROWS", tile[0])
-    monkeypatch.setenv("MOE_TILE_WAVES", tile[1])
-    h = int(tile[0])
+    h = tile[0]
     sizes = [h - 1, h, h + 1, 1, 0, 2 * h + 3]
     G, d, F = len(sizes), 128, 192
     offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
@@ -337,9 +327,9 @@ def test_group_sizes_around_tile_heights(tile, act, monkeypatch):
     if act == "gelu":
         du = None
     say(f"[case] expert FFN ({act}) group sizes {sizes} tile={tile}")
-    y = B.expert_ffn(dx, off_t, dg, du, dd, R, act=act).clone()
+    y = B.expert_ffn(dx, off_t, dg, du, dd, R, act=act, tile=tile).clone()
     y_p = B.expert_ffn(dx, off_t, B.pack_weights(dg), None if du is None else B.pack_weights(du),
-                       B.pack_weights(dd), R, act=act, packed=True).clone()
+                       B.pack_weights(dd), R, act=act, packed=True, tile=tile).clone()
     torch.cuda.synchronize()
     assert torch.equal(y_p.view(torch.int32), y.view(torch.int32))
     x64 = x.double().numpy()
@@ -425,10 +415,31 @@ def test_empty_batch_is_noop():
     assert out.shape == (0, cfg.d)
 
 
-# ---- the five workloads at full size (routing on every token, outputs sampled) ----
-# sampled output tokens per full-size workload (None: every token)
-SAMPLES = {"prefill-e64": 8, "shared-routed-e16": 10, "capacity-e16": 12, "decode-e64": None,
-           "capacity-e16-slot-reroute": 12, "capacity-e16-reroute": 12, "wide-e384-top6-shared": 4, "wide-e128-top2": 8}
+# ---- the workloads at full size: routing and dispatch on every token; outputs on the
+# tokens that hold the first and last row of every M-tile of every group (the tile height
+# the layer's own plan picks), every token for decode, random samples for the wide shapes
+# (hundreds of experts: the oracle would regenerate all of them) ----
+# "tiles": tile-boundary tokens; an int: that many random tokens; None: every token
+SAMPLES = {"prefill-e64": "tiles", "shared-routed-e16": "tiles", "capacity-e16": "tiles", "decode-e64": None,
+           "capacity-e16-slot-reroute": "tiles", "capacity-e16-reroute": "tiles",
+           "capacity-e16-calibrated": "tiles", "wide-e384-top6-shared": 4, "wide-e128-top2": 8}
+
+
+def tile_boundary_tokens(cfg, res, bm):
+    """Tokens whose slots hold the first and last row of every M-tile (bm rows) of every
+    routed group and of the shared group (rows = tokens) -> (tokens, number of tiles)."""
+    offs, perm, k = res["offsets"], res["perm"], cfg.k
+    toks, tiles = set(), 0
+    for g in range(cfg.E):
+        for m0 in range(int(offs[g]), int(offs[g + 1]), bm):
+            m1 = min(m0 + bm, int(offs[g + 1])) - 1
+            toks.update((int(perm[m0]) // k, int(perm[m1]) // k))
+            tiles += 1
+    if cfg.shared:
+        for m0 in range(0, cfg.T, bm):
+            toks.update((m0, min(m0 + bm, cfg.T) - 1))
+            tiles += 1
+    return np.array(sorted(toks)), tiles
 FULL = {n: BY_NAME[n] for n in ("prefill-e64", "shared-routed-e16", "capacity-e16", "decode-e64",
                                 "wide-e384-top6-shared", "wide-e128-top2")}
 # the capacity workload with first choices first and overflow re-routed
@@ -436,6 +447,13 @@ FULL["capacity-e16-slot-reroute"] = BY_NAME["capacity-e16"].scaled(name="capacit
                                                                    priority="slot", overflow="reroute")
 # and with token-major priority (a token's overflowed slots are adjacent in the list)
 FULL["capacity-e16-reroute"] = BY_NAME["capacity-e16"].scaled(name="capacity-e16-reroute", overflow="reroute")
+# the capacity workload with offsets calibrated to the 5-20% drop regime, all three policies
+FULL["capacity-e16-calibrated"] = BY_NAME["capacity-e16-calibrated"]
+FULL["capacity-e16-calibrated-slot-reroute"] = BY_NAME["capacity-e16-calibrated"].scaled(
+    name="capacity-e16-calibrated-slot-reroute", priority="slot", overflow="reroute")
+FULL["capacity-e16-calibrated-slot"] = BY_NAME["capacity-e16-calibrated"].scaled(
+    name="capacity-e16-calibrated-slot", priority="slot")
+SAMPLES["capacity-e16-calibrated-slot-reroute"] = SAMPLES["capacity-e16-calibrated-slot"] = "tiles"
 
 
 @pytest.mark.parametrize("name", list(FULL))
@@ -456,7 +474,11 @@ def test_workload_full_size(name):
     assert res["counts"].sum() == cfg.T * cfg.k
     n = SAMPLES[name]
     tokens = None
-    if n is not None:
+    if n == "tiles":
+        plan = layer_for(cfg, inp).plan(cfg.T)
+        tokens, rep["tiles_covered"] = tile_boundary_tokens(cfg, res, plan["tile_rows"])
+        rep["tile_rows"], rep["tokens_checked"] = plan["tile_rows"], len(tokens)
+    elif n is not None:
         rng = np.random.default_rng(cfg.seed)
         tokens = np.sort(rng.choice(np.nonzero(~flip)[0], size=n, replace=False))
     check_output(cfg, x64, z_o, res, expert_fetcher(cfg, inp), shared_weights(inp), tokens, rep)
