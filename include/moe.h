@@ -335,6 +335,26 @@ moe_status_t moe_layer_plan(const moe_layer_args_t* a, moe_ffn_plan_t* plan);
  */
 moe_status_t moe_layer_forward(const moe_layer_args_t* a, hipStream_t stream);
 
+/* Size of the fixed device scratch of moe_layer_forward_noalloc, per GPU. */
+#define MOE_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * moe_layer_forward_noalloc - moe_layer_forward for callers that cannot allocate device
+ *   memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ *   hipMalloc): the same kernels and results (bit-identical), but the workspace is a
+ *   fixed array of MOE_SCRATCH_BYTES inside the library, one per GPU, held until the
+ *   process ends.  a->ws and a->ws_bytes are ignored; the caller still passes every input
+ *   and output.  The call allocates and frees nothing.
+ *   Limit: moe_layer_workspace_bytes(a) <= MOE_SCRATCH_BYTES, else MOE_EWORKSPACE before
+ *   any launch (at d = 4096, F = 14336, k = 2 about 700 tokens per call: decode-sized
+ *   batches).  Invalid arguments: as moe_layer_forward.  The first call on a device looks
+ *   up that device's array (hipGetSymbolAddress; MOE_EHIP if that fails).
+ *   Every call on one GPU uses the same array, and each call overwrites it: calls that
+ *   overlap in time on one GPU (other streams, or other host threads without ordering)
+ *   race and give undefined results.  Calls ordered on one stream are safe.
+ */
+moe_status_t moe_layer_forward_noalloc(const moe_layer_args_t* a, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,6 +23,7 @@ WEIGHT_MODES = {"renormalized": 0, "softmax": 1}
 PRIORITIES = {"token": 0, "slot": 1}
 OVERFLOWS = {"drop": 0, "reroute": 1}
 MOE_LAYOUT_LINEAR, MOE_LAYOUT_PACKED = 0, 1
+MOE_SCRATCH_BYTES = 64 << 20          # the fixed scratch of moe_layer_forward_noalloc, per GPU
 STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EUNSUPPORTED", 3: "MOE_EWORKSPACE", 4: "MOE_EHIP"}
 
 # entry points declared in include/moe.h
@@ -30,7 +31,7 @@ EXPORTS = ("moe_status_string", "moe_last_error", "moe_route_workspace_bytes", "
            "moe_capacity", "moe_dispatch_workspace_bytes",
            "moe_dispatch", "moe_pack_weights", "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine",
            "moe_routing_stats_workspace_bytes", "moe_routing_stats",
-           "moe_layer_workspace_bytes", "moe_layer_plan", "moe_layer_forward")
+           "moe_layer_workspace_bytes", "moe_layer_plan", "moe_layer_forward", "moe_layer_forward_noalloc")
 
 
 class MoEError(RuntimeError):
@@ -117,6 +118,8 @@ def lib():
         L.moe_layer_plan.argtypes = [C.POINTER(LayerArgs), C.POINTER(FfnPlan)]
         L.moe_layer_forward.restype = C.c_int
         L.moe_layer_forward.argtypes = [C.POINTER(LayerArgs), vp]
+        L.moe_layer_forward_noalloc.restype = C.c_int
+        L.moe_layer_forward_noalloc.argtypes = [C.POINTER(LayerArgs), vp]
         _lib = L
     return _lib
 
@@ -292,13 +295,15 @@ class Layer:
     capacity_factor: if given, the capacity of each call is capacity_rule(T, k, E,
     capacity_factor, min_capacity) for its T tokens (instead of the fixed `capacity`).
     tile: (rows per M-tile, waves) of the expert FFN, or None for the automatic choice.
+    noalloc=True: forward() calls moe_layer_forward_noalloc, which runs on the library's
+    fixed device scratch (MOE_SCRATCH_BYTES per GPU) instead of a workspace tensor.
     """
 
     def __init__(self, w_r, w_gate, w_up, w_down, k, act="swiglu", bias=None, capacity=0,
                  s_gate=None, s_up=None, s_down=None, out_dtype=torch.float32, stats=False,
                  lambda_balance=0.01, lambda_aux=0.01, gamma_aux=100.0, weights="renormalized",
                  priority="token", overflow="drop", packed=False, prepacked=False, capacity_factor=None,
-                 min_capacity=0, tile=None):
+                 min_capacity=0, tile=None, noalloc=False):
         self.w_r, self.bias = w_r, bias
         self.w_gate, self.w_up, self.w_down = w_gate, w_up, w_down
         self.s_gate, self.s_up, self.s_down = s_gate, s_up, s_down
@@ -313,6 +318,7 @@ class Layer:
         self.overflow = OVERFLOWS[overflow]
         self.stat_coeffs = (lambda_balance, lambda_aux, gamma_aux)
         self.tile = (0, 0) if tile is None else (int(tile[0]), int(tile[1]))
+        self.noalloc = bool(noalloc)
         self.act = MOE_ACT_SWIGLU if act == "swiglu" else MOE_ACT_GELU
         self.E = w_r.shape[1]
         self.F, self.d = w_gate.shape[1], w_gate.shape[2]
@@ -378,7 +384,7 @@ class Layer:
         self.n_dropped = torch.empty(1, dtype=torch.int32, device=dev)
         if self.want_stats:
             self.stats = torch.empty(5 + self.E, dtype=torch.float32, device=dev)
-        self.ws = _ws(lib().moe_layer_workspace_bytes(C.byref(self._args(x))), dev)
+        self.ws = None if self.noalloc else _ws(lib().moe_layer_workspace_bytes(C.byref(self._args(x))), dev)
         self._T, self._dev, self._dtype = T, dev, x.dtype
 
     def forward(self, x, stage_events=None):
@@ -391,13 +397,15 @@ class Layer:
         a.topk_idx, a.topk_w, a.logits = _ptr(self.topk_idx), _ptr(self.topk_w), _ptr(self.logits)
         a.counts, a.offsets, a.perm = _ptr(self.counts), _ptr(self.offsets), _ptr(self.perm)
         a.inv, a.n_dropped = _ptr(self.inv), _ptr(self.n_dropped)
-        a.ws, a.ws_bytes = _ptr(self.ws), self.ws.numel()
+        if self.ws is not None:
+            a.ws, a.ws_bytes = _ptr(self.ws), self.ws.numel()
         if stage_events is not None:
             if len(stage_events) != STAGE_EVENTS:
                 raise ValueError(f"need {STAGE_EVENTS} events")
             arr = (C.c_void_p * STAGE_EVENTS)(*[ev.cuda_event for ev in stage_events])
             a.stage_events = C.cast(arr, C.POINTER(C.c_void_p))
-        _check(lib().moe_layer_forward(C.byref(a), _stream(x.device)))
+        fwd = lib().moe_layer_forward_noalloc if self.noalloc else lib().moe_layer_forward
+        _check(fwd(C.byref(a), _stream(x.device)))
         return self.out
 
     __call__ = forward

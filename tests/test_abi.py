@@ -266,3 +266,20 @@ def test_layer_validation_and_workspace(lib):
     with_shared.T = 4096
     with_shared.s_gate = with_shared.s_up = with_shared.s_down = 256
     assert lib.moe_layer_workspace_bytes(C.byref(with_shared)) > need
+
+
+def test_noalloc_rejects_before_any_launch(lib):
+    """moe_layer_forward_noalloc checks its arguments and the fixed scratch's size on the
+    host: a prefill-sized call needs more than MOE_SCRATCH_BYTES and is refused with
+    MOE_EWORKSPACE, bad sizes with MOE_EINVAL, before any HIP call (no GPU here)."""
+    a = _layer_args(T=4096)
+    for f in ("x", "w_r", "w_gate", "w_up", "w_down", "out"):
+        setattr(a, f, 256)
+    assert lib.moe_layer_workspace_bytes(C.byref(a)) > B.MOE_SCRATCH_BYTES
+    assert lib.moe_layer_forward_noalloc(C.byref(a), None) == 3
+    assert b"scratch" in lib.moe_last_error()
+    a.k = 65
+    assert lib.moe_layer_forward_noalloc(C.byref(a), None) == 1
+    assert lib.moe_layer_forward_noalloc(None, None) == 1
+    small = _layer_args(T=16)                      # a decode batch fits the scratch
+    assert 0 < lib.moe_layer_workspace_bytes(C.byref(small)) <= B.MOE_SCRATCH_BYTES
