@@ -68,7 +68,7 @@ def test_workload_table():
     assert BY_NAME["shared-routed-e16"].shared and BY_NAME["wide-e384-top6-shared"].shared
     assert BY_NAME["decode-e64"].T == 16
     cal = BY_NAME["capacity-e16-calibrated"]
-    assert (cal.T, cal.E, cal.k, cal.capacity) == (1024, 16, 2, 128) and cal.bias_var == 0.25 ** 2
+    assert (cal.T, cal.E, cal.k, cal.capacity) == (1024, 16, 2, 128) and cal.bias_var == 0.0225
 
 
 def test_bench_rejects_several_gpus():
