@@ -41,6 +41,8 @@ def parse():
                     help="workload number 1-8 (default 2: prefill, E=64; the decode workload, 5, is then "
                          "measured in the same run and reported as the `decode` object)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workload of the default run")
+    ap.add_argument("--tile", default=None, metavar="ROWS,WAVES",
+                    help="explicit tile of the expert FFN (moe_tile_t), e.g. 256,4; default: the library's choice")
     ap.add_argument("--priority", choices=("token", "slot"), default=None,
                     help="capacity priority (default: the workload's, token-major)")
     ap.add_argument("--overflow", choices=("drop", "reroute"), default=None,
@@ -187,7 +189,7 @@ def cpu_baseline(cfg, inp, L, n_exp):
                 seconds=round(t_oracle, 2))
 
 
-def load_layer(cfg, packed):
+def load_layer(cfg, packed, tile=None):
     """Seeded inputs of the workload on cuda:0 and its layer (expert weights packed once at
     load time, one tensor at a time, each linear copy freed once its packed copy exists)."""
     import torch
@@ -203,7 +205,7 @@ def load_layer(cfg, packed):
                 torch.cuda.empty_cache()
     L = B.Layer(inp["w_r"], inp["w_gate"], inp["w_up"], inp["w_down"], cfg.k, act=cfg.act, bias=inp["bias"],
                 capacity=cfg.capacity, s_gate=inp["s_gate"], s_up=inp["s_up"], s_down=inp["s_down"],
-                weights=cfg.weights, priority=cfg.priority, overflow=cfg.overflow, prepacked=packed)
+                weights=cfg.weights, priority=cfg.priority, overflow=cfg.overflow, prepacked=packed, tile=tile)
     return inp, L
 
 
@@ -251,7 +253,8 @@ def measure(cfg, args, packed, graph):
     """One workload: tokens/s, the rooflines of its GEMMs and of the whole step, routing
     facts, and (unless disabled) the oracle baseline."""
     import torch
-    inp, L = load_layer(cfg, packed)
+    tile = tuple(int(v) for v in args.tile.split(",")) if args.tile else None
+    inp, L = load_layer(cfg, packed, tile)
     elapsed, stage_ms = time_layer(cfg, L, inp["x"], args.steps, args.warmup, graph)
     ms_step = elapsed / args.steps * 1e3
     kept, touched, rows = layer_counts(cfg, L)

@@ -37,8 +37,11 @@
  *     per-row expert outputs y are always fp32.
  *   - Requirements: T >= 0 (T == 0 is a no-op), d >= 1, 1 <= E <= 1024,
  *     1 <= k <= E, F >= 1; for MOE_BF16 expert FFNs, d and F must be multiples of 64,
- *     and MOE_BF16 routing with d not a multiple of 32 takes at most 888 experts
- *     (MOE_EUNSUPPORTED otherwise).  Pointers must be 16-byte aligned.
+ *     the hidden states x (T x d bf16) and one expert matrix (F x d bf16) must each stay
+ *     below 2 GiB (at d = 4096: up to 262143 tokens per call; the hidden activation and
+ *     the expert outputs, which grow with T k F, have no such limit), and MOE_BF16
+ *     routing with d not a multiple of 32 takes at most 888 experts (MOE_EUNSUPPORTED
+ *     otherwise).  Pointers must be 16-byte aligned.
  *   - Calls on the same stream are ordered; concurrent calls on different streams
  *     share no library state.
  *   - Graph capture: the compute calls enqueue kernels only (no allocation, memset,
@@ -206,7 +209,8 @@ size_t moe_expert_ffn_workspace_bytes(int64_t max_rows, int32_t G, int64_t d, in
  *   expert are computed together.  GeLU expert: y = W2 gelu(W1 x) with w_gate = W1
  *   [G,F,d], w_down = W2 [G,d,F], w_up = NULL.  SwiGLU expert:
  *   y = Wd (silu(Wg x) * (Wu x)) with w_gate = Wg, w_up = Wu [G,F,d], w_down = Wd.
- *   x        [n_x, d] dtype dt
+ *   x        [n_x, d] dtype dt (bf16: below 2 GiB; without perm n_x >= max_rows is checked,
+ *            with perm every row perm[r] / k it names must lie inside those 2 GiB)
  *   perm     NULL: row r reads x[r];  else row r reads x[perm[r] / k]
  *   offsets  [G+1] int32 (device): group g owns rows [offsets[g], offsets[g+1]),
  *            non-decreasing, offsets[0] >= 0.  Rows at or beyond max_rows are ignored.

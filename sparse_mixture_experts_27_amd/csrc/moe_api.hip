@@ -81,13 +81,17 @@ moe_status_t check_route_args(const void* x, const void* w_r, int dt, int64_t T,
   return MOE_OK;
 }
 
-// The bf16 kernels address each operand (x or H rows, one expert's weights) with 32-bit
-// byte offsets below 2^31.
-moe_status_t check_bf16_operands(int64_t max_rows, int64_t d, int64_t F) {
+// The bf16 kernels address the hidden states x (rows gathered anywhere in it) and one
+// expert's weights with 32-bit byte offsets from their start, so each must stay below 2 GiB;
+// the hidden activation H is addressed from each tile's first row and has no such limit.
+moe_status_t check_bf16_operands(int64_t x_rows, int64_t d, int64_t F) {
   constexpr int64_t kMaxOperand = (int64_t{1} << 31) - 1;
-  if (max_rows * d * 2 > kMaxOperand || max_rows * F * 2 > kMaxOperand || F * d * 2 > kMaxOperand)
-    return fail(MOE_EUNSUPPORTED, "bf16 expert FFN operands must stay below 2 GiB (rows=%lld d=%lld F=%lld); "
-                "split the batch", (long long)max_rows, (long long)d, (long long)F);
+  if (x_rows * d * 2 > kMaxOperand)
+    return fail(MOE_EUNSUPPORTED, "bf16 hidden states x must stay below 2 GiB (%lld rows x d=%lld); "
+                "split the batch", (long long)x_rows, (long long)d);
+  if (F * d * 2 > kMaxOperand)
+    return fail(MOE_EUNSUPPORTED, "one bf16 expert matrix must stay below 2 GiB (F=%lld d=%lld)", (long long)F,
+                (long long)d);
   return MOE_OK;
 }
 
@@ -106,7 +110,7 @@ moe_status_t check_tile(const moe_tile_t* t) {
 int tile_rows_of(const moe_tile_t* t) { return t ? t->rows : 0; }
 int tile_waves_of(const moe_tile_t* t) { return t ? t->waves : 0; }
 
-moe_status_t check_ffn_args(const void* x, const int32_t* offsets, int G, int64_t max_rows, int64_t d,
+moe_status_t check_ffn_args(const void* x, const int32_t* perm, const int32_t* offsets, int G, int64_t max_rows, int64_t d,
                             int64_t F, int act, int dt, const void* w_gate, const void* w_up,
                             const void* w_down, const void* y) {
   if (!valid_dt(dt)) return fail(MOE_EINVAL, "dtype %d is not MOE_F32 or MOE_BF16", dt);
@@ -118,7 +122,9 @@ moe_status_t check_ffn_args(const void* x, const int32_t* offsets, int G, int64_
     return fail(MOE_EUNSUPPORTED, "bf16 expert FFN needs d and F multiples of 64 (d=%lld F=%lld)",
                 (long long)d, (long long)F);
   if (dt == MOE_BF16) {
-    if (moe_status_t st = check_bf16_operands(max_rows, d, F)) return st;
+    // without a permutation row r reads x[r]: x holds max_rows rows; with one, the rows of
+    // x it names must lie inside the first 2 GiB of x (its row count is not an argument)
+    if (moe_status_t st = check_bf16_operands(perm ? 0 : max_rows, d, F)) return st;
   }
   if (!x || !offsets || !w_gate || !w_down || !y) return fail(MOE_EINVAL, "moe_expert_ffn: null required pointer");
   if (act == MOE_ACT_SWIGLU && !w_up) return fail(MOE_EINVAL, "SwiGLU needs w_up");
@@ -233,7 +239,8 @@ moe_status_t moe_expert_ffn(const void* x, const int32_t* perm, int32_t k, const
                             moe_layout_t layout, const void* w_gate, const void* w_up, const void* w_down, float* y,
                             const moe_tile_t* tile, void* ws, size_t ws_bytes, hipStream_t stream) {
   g_last_error[0] = 0;
-  if (moe_status_t st = check_ffn_args(x, offsets, G, max_rows, d, F, act, dt, w_gate, w_up, w_down, y)) return st;
+  if (moe_status_t st = check_ffn_args(x, perm, offsets, G, max_rows, d, F, act, dt, w_gate, w_up, w_down, y))
+    return st;
   if (moe_status_t st = check_layout(layout, dt)) return st;
   if (moe_status_t st = check_tile(tile)) return st;
   if (perm && k < 1) return fail(MOE_EINVAL, "k must be >= 1 when perm is given");
@@ -338,7 +345,7 @@ static moe_status_t check_layer_sizes(const moe_layer_args_t* a) {
   if (a->dt == MOE_BF16 && (a->d % 64 != 0 || a->F % 64 != 0))
     return fail(MOE_EUNSUPPORTED, "bf16 layer needs d and F multiples of 64");
   if (a->dt == MOE_BF16) {
-    if (moe_status_t st = check_bf16_operands(a->T * a->k + (a->s_gate ? a->T : 0), a->d, a->F)) return st;
+    if (moe_status_t st = check_bf16_operands(a->T, a->d, a->F)) return st;
   }
   return check_tile(&a->tile);
 }
@@ -385,7 +392,7 @@ moe_status_t moe_layer_forward(const moe_layer_args_t* a, hipStream_t stream) {
     if (p && !aligned16(p)) return fail(MOE_EINVAL, "weights and out must be 16-byte aligned");
   if (a->T == 0) return MOE_OK;
   if (a->dt == MOE_BF16) {
-    if (moe_status_t st = check_bf16_operands(a->T * a->k + (a->s_gate ? a->T : 0), a->d, a->F)) return st;
+    if (moe_status_t st = check_bf16_operands(a->T, a->d, a->F)) return st;
   }
   const size_t need = moe_layer_workspace_bytes(a);
   if (!a->ws || a->ws_bytes < need)

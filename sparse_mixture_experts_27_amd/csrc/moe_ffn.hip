@@ -182,9 +182,17 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& p, int bm, TileInfo&
 }
 
 // Raw buffer resource over [base, base + 2^31): every offset the GEMM forms is below 2^31
-// (the host rejects larger operands), so the range check never triggers.
+// (x and one expert's weights are below 2 GiB, checked on the host; H is addressed from
+// each tile's first row), so the range check only ever refuses deliberate out-of-range
+// offsets.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), 0x7FFFFFFF, 0x00020000);
+}
+
+// First row of the A operand's buffer resource: the tile's first row for the down
+// projection (A = H, read row by row), row 0 for the up projection (A = x, rows gathered).
+__device__ __forceinline__ int64_t a_base_row(int mode, const TileInfo& ti) {
+  return mode == MODE_DOWN ? ti.row_begin : 0;
 }
 
 // Source row of the A operand for output row r of group g.
@@ -278,7 +286,10 @@ __device__ __forceinline__ void ffn_gemm_bf16_body(const GemmArgs& p, uint16_t* 
   // ---- activation chunks loaded by this thread: chunk q = i*NT + tid -> row q/8 (mod
   // the tile height; a repeated row writes identical bytes), 16-byte column q%8 = tid%8.
   // The XOR swizzle uses row%8 = (tid/8)%8 for every i (NT/8 is a multiple of 8).
-  const char* Ab = reinterpret_cast<const char*>(p.a);
+  // H (the down projection's A) is addressed from the tile's first row, so its offsets stay
+  // below 2^31 however many rows H has; x is addressed from its start (gathered rows).
+  const int64_t a_row0 = a_base_row(MODE, ti);
+  const char* Ab = reinterpret_cast<const char*>(p.a) + a_row0 * p.K * 2;
   const int chunk = tid & 7;
   uint32_t aoff[AR];
 #pragma unroll
@@ -286,7 +297,7 @@ __device__ __forceinline__ void ffn_gemm_bf16_body(const GemmArgs& p, uint16_t* 
     const int r = WRAP ? ((i * NT + tid) >> 3) % BMT : (i * NT + tid) >> 3;
     const int rr = r < ti.nrows ? r : 0;    // padding rows repeat row 0 of the tile
     const int cc = WRAP ? chunk : (chunk ^ (r & 7));
-    aoff[i] = static_cast<uint32_t>((a_source_row(p, MODE, ti.g, ti.row_begin + rr) * p.K + k_begin +
+    aoff[i] = static_cast<uint32_t>(((a_source_row(p, MODE, ti.g, ti.row_begin + rr) - a_row0) * p.K + k_begin +
                                      cc * 8) * 2);
   }
   // Buffer resources: uniform base + 32-bit per-lane offset + uniform stage offset.
@@ -564,6 +575,220 @@ __global__ __launch_bounds__(NW * 64, 1) void ffn_gemm_bf16_kernel(GemmArgs p) {
   ffn_gemm_bf16_body<MODE, MT, NW, PK>(p, As0, As1, As2, As3);
 }
 
+// ---- wide tile: 256 rows x 256 MFMA columns, 4 waves in a 2 x 2 grid ------------------
+// For groups of many rows (the MFMA-bound shapes).  Wave (wm, wn) owns rows 128 wm ..
+// 128 wm + 127 and MFMA columns 128 wn .. 128 wn + 127 of the tile: 8 x 8 blocks of
+// 16 x 16, so each operand fragment it reads from LDS feeds 8 MFMAs (the 8-wave tile above
+// feeds 2 per activation fragment).  Both operands are staged through LDS by
+// buffer-to-LDS loads, stored in MFMA fragment order: a 16-row x 32-K fragment is one
+// KiB whose 16-byte chunk l is what lane l of the 16x16x32 operand holds (row l % 16,
+// K 8 (l / 16) .. +7), so every fragment read is one conflict-free ds_read_b128 and
+// no swizzle is needed.  K advances 32 per stage through WS LDS slots of 32 KiB (A and
+// B); every wave loads 4 A and 4 B fragments of each stage.  Stage s is multiplied in
+// two halves; between them each wave waits for its own loads of stage s+1, a barrier
+// publishes them, the loads of stage s+WS-1 go into the slot stage s-1 used (every wave
+// has finished reading it), and the fragments of stage s+1 are read into the second
+// register set while the second half of the MFMAs runs.  Padding rows of a partial tile
+// get an offset past the buffer's range: the load returns zeros without touching
+// memory, and their 16-row fragments are not multiplied.
+constexpr int WIDE_SLOTS = 4;                  // LDS slots (stages in flight: slots - 1)
+constexpr int WIDE_UNROLL = 4;                 // stages per loop iteration (a multiple of the slots and of 2)
+constexpr int WIDE_FRAG = 512;                 // bf16 elements per 16 x 32 fragment
+constexpr uint32_t OOB_OFFSET = 0x80000000u;   // beyond the 2^31 - 1 byte buffer range
+
+// Wait until at most N vector-memory loads of this wave are outstanding (s_waitcnt
+// immediate, gfx9 layout: vmcnt in [3:0] and [15:14]; expcnt and lgkmcnt at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int MODE, bool PK, int WS, int UNR>
+__device__ __forceinline__ void ffn_gemm_wide_body(const GemmArgs& p, uint16_t* __restrict__ S0,
+                                                   uint16_t* __restrict__ S1, uint16_t* __restrict__ S2,
+                                                   uint16_t* __restrict__ S3, uint16_t* __restrict__ S4,
+                                                   uint16_t* __restrict__ S5) {
+  static_assert(WS >= 3 && WS <= 6 && UNR % WS == 0 && UNR % 2 == 0, "slots and unroll");
+  auto slot_ptr = [&](int slot) -> uint16_t* {
+    return slot == 0 ? S0 : slot == 1 ? S1 : slot == 2 ? S2 : slot == 3 ? S3 : slot == 4 ? S4 : S5;
+  };
+  TileInfo ti;
+  if (!decode_tile(p, 256, ti)) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches and resources
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nmf = (ti.nrows + 15) >> 4;
+
+  int64_t k_begin = 0, k_end = p.K;
+  if (MODE == MODE_DOWN && p.splits > 1) {
+    k_begin = static_cast<int64_t>(ti.split) * p.k_chunk;
+    k_end = k_begin + p.k_chunk < p.K ? k_begin + p.k_chunk : p.K;
+  }
+  const int nst = k_end > k_begin ? static_cast<int>((k_end - k_begin) / 32) : 0;
+
+  // ---- A: fragments 4 wave + q of the tile (rows 16 f + lane % 16, K chunk lane / 16)
+  const int kc = lane >> 4;
+  const int64_t a_row0 = a_base_row(MODE, ti);
+  uint32_t aoff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = 16 * (4 * wave + q) + (lane & 15);
+    aoff[q] = r < ti.nrows ? static_cast<uint32_t>(((a_source_row(p, MODE, ti.g, ti.row_begin + r) - a_row0) * p.K +
+                                                    k_begin + 8 * kc) * 2)
+                           : OOB_OFFSET;
+  }
+  // ---- B: weight-row fragments 4 wave + q of the tile's 256 MFMA columns.  SwiGLU: the
+  // columns are [gate u0..u0+63 | up u0..u0+63 | gate u0+64.. | up u0+64..], u0 = 128 ntile,
+  // so wave wn's 128 columns hold the gate and up rows of the same 64 hidden units;
+  // fragment f = 4 wave + q is a gate fragment for even waves, an up fragment for odd ones.
+  const bool shared_grp = ti.g >= p.G;
+  const int64_t wstride = shared_grp ? 0 : static_cast<int64_t>(ti.g) * p.N * p.K;
+  const uint16_t* W0 = static_cast<const uint16_t*>(shared_grp ? p.sw0 : p.w0) + wstride;
+  const uint16_t* W1 = static_cast<const uint16_t*>(shared_grp ? p.sw1 : p.w1) + wstride;
+  const uint16_t* Wl = (MODE == MODE_SWIGLU_UP && (wave & 1)) ? W1 : W0;
+  uint32_t boff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    int64_t wrow;                              // first weight row of the fragment
+    if (MODE == MODE_SWIGLU_UP) wrow = static_cast<int64_t>(ti.ntile) * 128 + 64 * (wave >> 1) + 16 * q;
+    else wrow = static_cast<int64_t>(ti.ntile) * 256 + 16 * (4 * wave + q);
+    if (wrow >= p.N) wrow = 0;                 // past the last column: a valid row, not stored
+    if (PK)
+      boff[q] = static_cast<uint32_t>((((wrow >> 4) * (p.K >> 5) + (k_begin >> 5)) * 64 + lane) * 16);
+    else
+      boff[q] = static_cast<uint32_t>(((wrow + (lane & 15)) * p.K + k_begin + 8 * kc) * 2);
+  }
+  const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(p.a + a_row0 * p.K);
+  const __amdgpu_buffer_rsrc_t brsrc = make_rsrc(Wl);
+  constexpr int B_STAGE = PK ? 1024 : 64;      // bytes between the stages of one lane's weight chunk
+
+  // issue every load of stage st (clamped to the last stage: a repeated stage lands in a
+  // slot nobody reads again) into LDS slot `slot`: 4 A then 4 B fragments of this wave
+  auto issue = [&](int st, int slot) {
+    st = st < nst ? st : nst - 1;
+    uint16_t* base = slot_ptr(slot);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          arsrc, (__attribute__((address_space(3))) void*)(base + (4 * wave + q) * WIDE_FRAG), 16, aoff[q], st * 64, 0, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          brsrc, (__attribute__((address_space(3))) void*)(base + (16 + 4 * wave + q) * WIDE_FRAG), 16, boff[q],
+          st * B_STAGE, 0, 0);
+  };
+  auto barrier = [&]() {
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  };
+
+  f32x4 acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 ra[2][8], rb[2][8];
+  auto read = [&](int slot, int buf) {
+    const uint16_t* base = slot_ptr(slot);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      rb[buf][j] = *reinterpret_cast<const bf16x8*>(base + (16 + 8 * wn + j) * WIDE_FRAG + lane * 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      ra[buf][i] = *reinterpret_cast<const bf16x8*>(base + (8 * wm + i) * WIDE_FRAG + lane * 8);
+  };
+  // 4 row fragments (64 rows) x 8 column fragments; skipped as a whole (one uniform branch)
+  // when all 64 rows are padding
+  auto mfma_rows = [&](int buf, int i0) {
+    if (8 * wm + i0 < nmf) {
+#pragma unroll
+      for (int i = i0; i < i0 + 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[buf][i], rb[buf][j], acc[i][j], 0, 0, 0);
+    }
+  };
+  // One stage; its slot and register set are compile-time constants in the unrolled loop.
+  // The middle block runs on every stage, the last ones included (they read a slot that
+  // holds a repeated stage and issue clamped loads, both unused): a branch there would
+  // merge two wait states and make the compiler wait for every LDS read before the
+  // second half.  The next stage's fragments are read before the new loads are issued.
+  auto stage = [&](int st, int slot, int buf) {
+    mfma_rows(buf, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<8 * (WS - 3)>();                // stage st+1 (8 loads per stage; st+2 .. st+WS-2 may fly)
+    barrier();
+    read((slot + 1) % WS, buf ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(st + WS - 1, (slot + WS - 1) % WS);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_rows(buf, 4);
+  };
+  if (nst > 0) {
+#pragma unroll
+    for (int st = 0; st < WS - 1; ++st) issue(st, st);
+    wait_vmcnt<8 * (WS - 2)>();                // stage 0
+    barrier();
+    read(0, 0);
+    for (int base = 0;; base += UNR) {
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        if (base + u >= nst) goto wide_done;
+        stage(base + u, u % WS, u & 1);
+      }
+    }
+  }
+wide_done:
+  wait_vmcnt<0>();                             // no load into this workgroup's LDS outlives it
+
+  // ---- epilogue: C layout, lane holds rows 4 (lane / 16) + v of each 16 x 16 block, column lane % 16
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (8 * wm + i >= nmf) continue;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int r = 128 * wm + 16 * i + 4 * (lane >> 4) + v;
+      if (r >= ti.nrows) continue;
+      const int64_t orow = ti.row_begin + r;
+      if (MODE == MODE_SWIGLU_UP) {
+        uint16_t* H = static_cast<uint16_t*>(p.out);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t u = static_cast<int64_t>(ti.ntile) * 128 + 64 * wn + 16 * j + (lane & 15);
+          if (u < p.N) H[orow * p.N + u] = f32_to_bf16(silu_f(acc[i][j][v]) * acc[i][j + 4][v]);
+        }
+      } else if (MODE == MODE_GELU_UP) {
+        uint16_t* H = static_cast<uint16_t*>(p.out);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int64_t c = static_cast<int64_t>(ti.ntile) * 256 + 128 * wn + 16 * j + (lane & 15);
+          if (c < p.N) H[orow * p.N + c] = f32_to_bf16(gelu_f(acc[i][j][v]));
+        }
+      } else {
+        float* Y = static_cast<float*>(p.out) + static_cast<int64_t>(ti.split) * p.split_stride;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int64_t c = static_cast<int64_t>(ti.ntile) * 256 + 128 * wn + 16 * j + (lane & 15);
+          if (c < p.N) Y[orow * p.N + c] = acc[i][j][v];
+        }
+      }
+    }
+  }
+}
+
+template <int MODE, bool PK>
+__global__ __launch_bounds__(256, 1) void ffn_gemm_wide_kernel(GemmArgs p) {
+  // WIDE_SLOTS slots x (16 A + 16 B fragments) x 1 KiB
+  // (the slots are disjoint parts of one array, handed to the body as distinct restrict
+  // pointers so the compiler can tell the slot being read from the slots being filled)
+  constexpr int WS = WIDE_SLOTS;
+  constexpr int SLOT = 32 * WIDE_FRAG;
+  __shared__ __attribute__((aligned(1024))) uint16_t Sl[WS * SLOT];
+  ffn_gemm_wide_body<MODE, PK, WS, WIDE_UNROLL>(p, Sl, Sl + SLOT, Sl + 2 * SLOT, Sl + (WS > 3 ? 3 : 0) * SLOT,
+                                                Sl + (WS > 4 ? 4 : 0) * SLOT, Sl + (WS > 5 ? 5 : 0) * SLOT);
+}
+
 // Fragment packing of bf16 weights [G, N, K] (K contiguous): 16-byte chunk c of the
 // output, with c = ((g * N/16 + i) * K/32 + j) * 64 + l, holds the 8 elements of row
 // 16 i + l % 16 at K = 32 j + 8 (l / 16): the 64 lanes of one 16 x 32 MFMA operand
@@ -697,7 +922,7 @@ void launch_bf16_gemm_l(int bm, int nw, int64_t grid, const GemmArgs& g, hipStre
       case 32: ffn_gemm_bf16_kernel<MODE, 2, 4, PK><<<gr, 256, 0, s>>>(g); break;
       case 64: ffn_gemm_bf16_kernel<MODE, 4, 4, PK><<<gr, 256, 0, s>>>(g); break;
       case 128: ffn_gemm_bf16_kernel<MODE, 8, 4, PK><<<gr, 256, 0, s>>>(g); break;
-      case 256: ffn_gemm_bf16_kernel<MODE, 16, 4, PK><<<gr, 256, 0, s>>>(g); break;
+      case 256: ffn_gemm_wide_kernel<MODE, PK><<<gr, 256, 0, s>>>(g); break;   // 2 x 2 waves
       default: break;
     }
   }

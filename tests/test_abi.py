@@ -149,10 +149,18 @@ def test_ffn_validation(lib):
     f32_packed[17] = lib.moe_expert_ffn_workspace_bytes(8192, 64, 4096, 14336, B.MOE_ACT_SWIGLU, B.MOE_F32, None)
     assert lib.moe_expert_ffn(*f32_packed) == 1
     assert b"bf16" in lib.moe_last_error()
-    huge = list(base); huge[5] = 80000               # H = 80000 x 14336 bf16 rows > 2 GiB
-    huge[17] = lib.moe_expert_ffn_workspace_bytes(80000, 64, 4096, 14336, B.MOE_ACT_SWIGLU, B.MOE_BF16, None)
+    # without a permutation row r reads x[r]: 300000 rows of d = 4096 bf16 exceed 2 GiB
+    huge = list(base); huge[1] = None; huge[5] = 300000
+    huge[17] = lib.moe_expert_ffn_workspace_bytes(300000, 64, 4096, 14336, B.MOE_ACT_SWIGLU, B.MOE_BF16, None)
     assert lib.moe_expert_ffn(*huge) == 2
     assert b"2 GiB" in lib.moe_last_error()
+    # a hidden activation H of 80000 x 14336 bf16 (2.3 GB) is no limit: the call reaches the
+    # workspace check (one byte short)
+    big_h = list(base); big_h[5] = 80000
+    big_h[17] = lib.moe_expert_ffn_workspace_bytes(80000, 64, 4096, 14336, B.MOE_ACT_SWIGLU, B.MOE_BF16, None) - 1
+    assert lib.moe_expert_ffn(*big_h) == 3
+    wide_w = list(base); wide_w[7] = 262208          # one expert matrix F x d > 2 GiB
+    assert lib.moe_expert_ffn(*wide_w) == 2
 
 
 @pytest.mark.parametrize("rows,waves,ok", [(0, 0, True), (32, 16, True), (192, 8, True), (192, 0, True),

@@ -276,7 +276,7 @@ def test_pack_weights_layout(G, N, K):
 
 # explicit tiles (rows per M-tile, waves per workgroup); None = the plan's own choice;
 # (0, 4) = the automatic height with 4 waves (192 rows have no 4-wave kernel: 256 rows)
-TILES = [None, (256, 16), (192, 8), (0, 4), (128, 4), (64, 8), (32, 16)]
+TILES = [None, (256, 16), (256, 4), (192, 8), (0, 4), (128, 4), (64, 8), (32, 16)]
 
 
 @pytest.mark.parametrize("name", ["bf16-swiglu-multitile", "bf16-gelu", "bf16-shared-bias", "bf16-decode",
@@ -303,7 +303,7 @@ def test_tile_overrides_against_oracle(tile):
 
 # group sizes on both sides of a tile height (and of two tiles), a one-row group and an
 # empty group, for every tile shape the plan can pick
-EDGE_TILES = [(32, 8), (64, 8), (128, 8), (192, 8), (256, 8), (256, 16), (128, 4)]
+EDGE_TILES = [(32, 8), (64, 8), (128, 8), (192, 8), (256, 8), (256, 16), (256, 4), (128, 4)]
 
 
 @pytest.mark.parametrize("act", ["swiglu", "gelu"])
@@ -493,6 +493,34 @@ def test_workload_full_size(name):
     rep["l_balance"], rep["l_aux"], rep["entropy"] = sref["l_balance"], sref["l_aux"], sref["entropy"]
     say(f"[ok] {cfg.name}: {rep}")
     del inp
+    torch.cuda.empty_cache()
+
+
+def test_hidden_activation_beyond_2gib():
+    """A prefill batch whose hidden activation H (81920 rows x 14336 bf16 = 2.35 GB) and
+    expert outputs exceed 2 GiB: the down projection addresses H from each tile's first
+    row.  Routing and dispatch on every token; the output on the tokens holding the last
+    row of every M-tile of every group, against the oracle."""
+    cfg = MoEConfig("big-h", 44, T=40960, d=4096, E=8, k=2, F=14336, act="swiglu", dtype="bf16")
+    say(f"[case] {cfg.label}: generating inputs")
+    inp = synth.make_inputs(cfg, DEV)
+    L = layer_for(cfg, inp, packed=True)
+    plan = L.plan(cfg.T)
+    assert cfg.T * cfg.k * cfg.F * 2 > 2 ** 31
+    res = run_layer(cfg, inp, packed=True)
+    x64, wr64, b64 = _x64(inp)
+    rep = {}
+    z_o, _ = check_route(cfg, x64, wr64, b64, res, rep)
+    check_dispatch(cfg, res)
+    offs, perm, bm = res["offsets"], res["perm"], plan["tile_rows"]
+    last_rows = [min(m0 + bm, int(offs[g + 1])) - 1 for g in range(cfg.E)
+                 for m0 in range(int(offs[g]), int(offs[g + 1]), bm)]
+    tokens = np.unique(perm[np.array(last_rows)] // cfg.k)
+    beyond = int(np.sum(np.array(last_rows) * cfg.F * 2 >= 2 ** 31))
+    assert beyond > 0                                   # some checked rows lie past 2 GiB of H
+    check_output(cfg, x64, z_o, res, expert_fetcher(cfg, inp), None, tokens, rep)
+    say(f"[ok] {cfg.label}: {len(last_rows)} M-tiles ({beyond} past 2 GiB of H), {len(tokens)} tokens: {rep}")
+    del inp, L
     torch.cuda.empty_cache()
 
 
