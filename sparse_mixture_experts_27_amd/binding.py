@@ -13,8 +13,7 @@ from typing import Optional
 
 import torch
 
-# MOE_LIBRARY may name another build of the same library (e.g. a tuning variant).
-_LIB_PATH = os.environ.get("MOE_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 _lib = None
 
 MOE_F32, MOE_BF16 = 0, 1

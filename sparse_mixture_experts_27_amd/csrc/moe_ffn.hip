@@ -185,6 +185,8 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& p, int bm, TileInfo&
 // (x and one expert's weights are below 2 GiB, checked on the host; H is addressed from
 // each tile's first row), so the range check only ever refuses deliberate out-of-range
 // offsets.
+constexpr uint32_t OOB_OFFSET = 0x80000000u;   // beyond the 2^31 - 1 byte buffer range
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), 0x7FFFFFFF, 0x00020000);
 }
@@ -209,9 +211,10 @@ __device__ __forceinline__ int64_t a_source_row(const GemmArgs& p, int mode, int
 // WRING-1 stages are in flight).  Activations: buffer-to-LDS loads D stages ahead into a
 // ring of D+1 LDS slots (when the tile has at least one 16-byte chunk per thread; smaller
 // tiles go through a 2-slot register ring and LDS stores, two stages ahead).  Every global load
-// is unconditional (padding rows read a valid row of the tile and inactive waves read
-// valid weight rows; neither result is stored) so the memory counters stay in step
-// across waves, and activation loads are issued before weight loads so that waiting
+// is issued unconditionally (padding rows take an out-of-range offset, which returns zeros
+// without touching memory, and inactive waves read valid weight rows; neither result is
+// stored) so the memory counters stay in step across waves, and activation loads are
+// issued before weight loads so that waiting
 // for one stage's activations never waits for weights.  Loads are raw buffer loads:
 // uniform base, 32-bit per-lane offset, uniform stage offset.  The LDS slots arrive as
 // distinct restrict pointers so the compiler can tell a slot being read from the slots
@@ -295,10 +298,12 @@ __device__ __forceinline__ void ffn_gemm_bf16_body(const GemmArgs& p, uint16_t* 
 #pragma unroll
   for (int i = 0; i < AR; ++i) {
     const int r = WRAP ? ((i * NT + tid) >> 3) % BMT : (i * NT + tid) >> 3;
-    const int rr = r < ti.nrows ? r : 0;    // padding rows repeat row 0 of the tile
+    // padding rows get an offset past the buffer's range: the load returns zeros without
+    // touching memory (their rows are never stored), and still counts for the waits
     const int cc = WRAP ? chunk : (chunk ^ (r & 7));
-    aoff[i] = static_cast<uint32_t>(((a_source_row(p, MODE, ti.g, ti.row_begin + rr) - a_row0) * p.K + k_begin +
-                                     cc * 8) * 2);
+    aoff[i] = r < ti.nrows ? static_cast<uint32_t>(((a_source_row(p, MODE, ti.g, ti.row_begin + r) - a_row0) * p.K +
+                                                    k_begin + cc * 8) * 2)
+                           : OOB_OFFSET;
   }
   // Buffer resources: uniform base + 32-bit per-lane offset + uniform stage offset.
   const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(Ab);
@@ -594,7 +599,6 @@ __global__ __launch_bounds__(NW * 64, 1) void ffn_gemm_bf16_kernel(GemmArgs p) {
 constexpr int WIDE_SLOTS = 4;                  // LDS slots (stages in flight: slots - 1)
 constexpr int WIDE_UNROLL = 4;                 // stages per loop iteration (a multiple of the slots and of 2)
 constexpr int WIDE_FRAG = 512;                 // bf16 elements per 16 x 32 fragment
-constexpr uint32_t OOB_OFFSET = 0x80000000u;   // beyond the 2^31 - 1 byte buffer range
 
 // Wait until at most N vector-memory loads of this wave are outstanding (s_waitcnt
 // immediate, gfx9 layout: vmcnt in [3:0] and [15:14]; expcnt and lgkmcnt at their maxima).
