@@ -113,15 +113,16 @@ moe_status_t launch_combine(const float* y, int64_t y_rows, int nsplit, int64_t 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
-// Round-to-nearest-even fp32 -> bf16 (finite inputs; NaN stays NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
-}
+// fp32 -> bf16, round to nearest even: one v_cvt_pk_bf16_f32 (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f)); }
 
-__device__ __forceinline__ float silu_f(float v) { return v / (1.0f + __expf(-v)); }
+// SiLU v * sigmoid(v) = v / (1 + e^-v), with the hardware exp2 and reciprocal (each within
+// about 1 ulp of fp32; the result is rounded to bf16 or feeds an fp32 product): no IEEE
+// division sequence in the GEMM epilogues.  Large negative v: e^-v overflows to inf and
+// the reciprocal to 0, so the result is -0; large positive v: the reciprocal is 1.
+__device__ __forceinline__ float silu_f(float v) {
+  return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504088896341f * v));
+}
 __device__ __forceinline__ float gelu_f(float v) { return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f)); }
 
 }  // namespace moe

@@ -22,6 +22,7 @@
 // each XCD (blockIdx % 8) walks a contiguous range of tiles: the tiles of one expert
 // share its activation rows in that XCD's L2.
 #include "moe_common.h"
+#include <type_traits>
 
 namespace moe {
 namespace {
@@ -189,6 +190,53 @@ constexpr uint32_t OOB_OFFSET = 0x80000000u;   // beyond the 2^31 - 1 byte buffe
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), 0x7FFFFFFF, 0x00020000);
+}
+
+// ---- epilogue stores.  In the MFMA C layout a lane holds rows 4 (lane / 16) + v, v = 0..3,
+// of one column (lane % 16) of a 16 x 16 block, so a plain store writes 2 or 4 bytes per
+// lane.  The 4 lanes of a quad hold 4 adjacent columns of the same 4 rows: a 4 x 4
+// transpose inside the quad (two DPP swaps, at distance 2 then 1) leaves lane t of the quad
+// with row t, columns 0..3, so each lane writes one 8-byte (bf16) or 16-byte (fp32) store.
+// Every lane of the quad must be active.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t quad_swap2(uint32_t v) {   // lanes t <-> t ^ 2
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t quad_swap1(uint32_t v) {   // lanes t <-> t ^ 1
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// h[v] = rows v of this lane's column -> the 4 bf16 of row (lane % 4), columns 0..3 of the quad.
+__device__ __forceinline__ u32x2 quad_rows_bf16(const float h[4], int lane) {
+  const int t = lane & 3;
+  const uint32_t a = pack_bf16(h[0], h[1]), b = pack_bf16(h[2], h[3]);
+  const bool low = t < 2, odd = t & 1;
+  const uint32_t recv = quad_swap2(low ? b : a);
+  const uint32_t X = low ? a : recv;            // column t % 2 of rows r0, r0 + 1 (r0 = t & 2)
+  const uint32_t Y = low ? recv : b;            // column t % 2 + 2 of the same rows
+  // odd lanes hand over row r0 (low halves), even lanes row r0 + 1 (high halves)
+  const uint32_t r2 = quad_swap1(__builtin_amdgcn_perm(Y, X, odd ? 0x05040100u : 0x07060302u));
+  u32x2 o;
+  o.x = odd ? __builtin_amdgcn_perm(X, r2, 0x07060100u) : __builtin_amdgcn_perm(r2, X, 0x05040100u);
+  o.y = odd ? __builtin_amdgcn_perm(Y, r2, 0x07060302u) : __builtin_amdgcn_perm(r2, Y, 0x07060100u);
+  return o;
+}
+
+// The same for fp32 values: the 4 floats of row (lane % 4), columns 0..3 of the quad.
+__device__ __forceinline__ f32x4 quad_rows_f32(const f32x4& v, int lane) {
+  const int t = lane & 3;
+  const bool low = t < 2, odd = t & 1;
+  const float q0 = __uint_as_float(quad_swap2(__float_as_uint(low ? v[2] : v[0])));
+  const float q1 = __uint_as_float(quad_swap2(__float_as_uint(low ? v[3] : v[1])));
+  const float X0 = low ? v[0] : q0, X1 = low ? v[1] : q1;   // column t % 2
+  const float Y0 = low ? q0 : v[2], Y1 = low ? q1 : v[3];   // column t % 2 + 2
+  const float w0 = __uint_as_float(quad_swap1(__float_as_uint(odd ? X0 : X1)));
+  const float w1 = __uint_as_float(quad_swap1(__float_as_uint(odd ? Y0 : Y1)));
+  return odd ? f32x4{w0, X1, w1, Y1} : f32x4{X0, w0, Y0, w1};
 }
 
 // First row of the A operand's buffer resource: the tile's first row for the down
@@ -525,46 +573,54 @@ __device__ __forceinline__ void ffn_gemm_bf16_body(const GemmArgs& p, uint16_t* 
   }
 pipeline_done:
 
-  // ---- epilogue.  C layout: lane holds rows 4*(lane/16)+v of each 16x16 block, column lane%16.
+  // ---- epilogue.  C layout: lane holds rows 4*(lane/16)+v of each 16x16 block, column
+  // lane%16; after the quad transpose, row 4*(lane/16) + lane%4 and 4 columns from
+  // 4*((lane/4)%4).
   if (!wave_on) return;
+  const int qrow = 4 * (lane >> 4) + (lane & 3);
+  const int qcol = 4 * ((lane >> 2) & 3);
 #pragma unroll
   for (int mf = 0; mf < MT; ++mf) {
     if (mf < nmf) {
+      if (PAIRED) {                         // lanes 8..15 of each row group hold the up half
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = mf * 16 + 4 * (lane >> 4) + v;
-        if (PAIRED) {                       // lanes 8..15 of each row group hold the up half
+        for (int v = 0; v < 4; ++v) {
+          const int r = mf * 16 + 4 * (lane >> 4) + v;
           const float g = acc[mf][0][v];
           const float u = __shfl_xor(g, 8);
           if (r < ti.nrows && (lane & 8) == 0)
             static_cast<uint16_t*>(p.out)[(ti.row_begin + r) * p.N + col_base + (lane & 7)] = f32_to_bf16(silu_f(g) * u);
-          continue;
         }
-        if (r < ti.nrows) {
-          const int64_t orow = ti.row_begin + r;
-          if (MODE == MODE_SWIGLU_UP) {
-            uint16_t* H = static_cast<uint16_t*>(p.out);
+        continue;
+      }
+      const int r = mf * 16 + qrow;
+      const int64_t orow = ti.row_begin + r;
+      if (MODE == MODE_SWIGLU_UP) {
+        uint16_t* H = static_cast<uint16_t*>(p.out);
 #pragma unroll
-            for (int nf = 0; nf < NF / 2; ++nf) {
-              const int64_t f = col_base + nf * 16 + (lane & 15);
-              const float h = silu_f(acc[mf][nf][v]) * acc[mf][nf + NF / 2][v];
-              H[orow * p.N + f] = f32_to_bf16(h);
-            }
-          } else if (MODE == MODE_GELU_UP) {
-            uint16_t* H = static_cast<uint16_t*>(p.out);
+        for (int nf = 0; nf < NF / 2; ++nf) {
+          float h[4];
 #pragma unroll
-            for (int nf = 0; nf < NF; ++nf) {
-              const int64_t f = col_base + nf * 16 + (lane & 15);
-              H[orow * p.N + f] = f32_to_bf16(gelu_f(acc[mf][nf][v]));
-            }
-          } else {
-            float* Y = static_cast<float*>(p.out) + static_cast<int64_t>(ti.split) * p.split_stride;
+          for (int v = 0; v < 4; ++v) h[v] = silu_f(acc[mf][nf][v]) * acc[mf][nf + NF / 2][v];
+          const u32x2 o = quad_rows_bf16(h, lane);
+          if (r < ti.nrows) *reinterpret_cast<u32x2*>(&H[orow * p.N + col_base + nf * 16 + qcol]) = o;
+        }
+      } else if (MODE == MODE_GELU_UP) {
+        uint16_t* H = static_cast<uint16_t*>(p.out);
 #pragma unroll
-            for (int nf = 0; nf < NF; ++nf) {
-              const int64_t n = col_base + nf * 16 + (lane & 15);
-              Y[orow * p.N + n] = acc[mf][nf][v];
-            }
-          }
+        for (int nf = 0; nf < NF; ++nf) {
+          float h[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) h[v] = gelu_f(acc[mf][nf][v]);
+          const u32x2 o = quad_rows_bf16(h, lane);
+          if (r < ti.nrows) *reinterpret_cast<u32x2*>(&H[orow * p.N + col_base + nf * 16 + qcol]) = o;
+        }
+      } else {
+        float* Y = static_cast<float*>(p.out) + static_cast<int64_t>(ti.split) * p.split_stride;
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf) {
+          const f32x4 o = quad_rows_f32(acc[mf][nf], lane);
+          if (r < ti.nrows) *reinterpret_cast<f32x4*>(&Y[orow * p.N + col_base + nf * 16 + qcol]) = o;
         }
       }
     }
@@ -589,16 +645,19 @@ __global__ __launch_bounds__(NW * 64, 1) void ffn_gemm_bf16_kernel(GemmArgs p) {
 // KiB whose 16-byte chunk l is what lane l of the 16x16x32 operand holds (row l % 16,
 // K 8 (l / 16) .. +7), so every fragment read is one conflict-free ds_read_b128 and
 // no swizzle is needed.  K advances 32 per stage through WS LDS slots of 32 KiB (A and
-// B); every wave loads 4 A and 4 B fragments of each stage.  Stage s is multiplied in
-// two halves; between them each wave waits for its own loads of stage s+1, a barrier
-// publishes them, the loads of stage s+WS-1 go into the slot stage s-1 used (every wave
-// has finished reading it), and the fragments of stage s+1 are read into the second
-// register set while the second half of the MFMAs runs.  Padding rows of a partial tile
-// get an offset past the buffer's range: the load returns zeros without touching
-// memory, and their 16-row fragments are not multiplied.
+// B); every wave loads 4 A and 4 B fragments of each stage.  A stage opens with one wait
+// (this wave's loads of stage s+1 and its LDS reads of stage s) and one barrier, after
+// which slot s+1 is complete and slot s is free; its 64 MFMAs then run in 8 groups (one
+// row fragment each), and after each group the wave reads 2 fragments of stage s+1 into
+// the other register set and issues 1 load of stage s+WS into slot s.  With one wave per
+// SIMD nothing else fills the MFMA pipe while a wave issues memory instructions, so they
+// go between the MFMA groups rather than in bursts.  Padding rows of a partial tile get
+// an offset past the buffer's range: the load returns zeros without touching memory, and
+// their 16-row fragments are not multiplied (one uniform branch per fragment).
 constexpr int WIDE_SLOTS = 4;                  // LDS slots (stages in flight: slots - 1)
 constexpr int WIDE_UNROLL = 4;                 // stages per loop iteration (a multiple of the slots and of 2)
 constexpr int WIDE_FRAG = 512;                 // bf16 elements per 16 x 32 fragment
+constexpr int WIDE_READ_GROUPS = 8;            // the next stage's 16 LDS reads go after the first this many MFMA groups
 
 // Wait until at most N vector-memory loads of this wave are outstanding (s_waitcnt
 // immediate, gfx9 layout: vmcnt in [3:0] and [15:14]; expcnt and lgkmcnt at their maxima).
@@ -693,48 +752,50 @@ __device__ __forceinline__ void ffn_gemm_wide_body(const GemmArgs& p, uint16_t* 
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   bf16x8 ra[2][8], rb[2][8];
-  auto read = [&](int slot, int buf) {
+  // fragment r of a stage from LDS slot `slot` into register set `buf`: r < 8 the wave's
+  // column fragments, r >= 8 its row fragments
+  auto read_one = [&](int slot, int buf, int r) {
     const uint16_t* base = slot_ptr(slot);
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      rb[buf][j] = *reinterpret_cast<const bf16x8*>(base + (16 + 8 * wn + j) * WIDE_FRAG + lane * 8);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      ra[buf][i] = *reinterpret_cast<const bf16x8*>(base + (8 * wm + i) * WIDE_FRAG + lane * 8);
+    if (r < 8) rb[buf][r] = *reinterpret_cast<const bf16x8*>(base + (16 + 8 * wn + r) * WIDE_FRAG + lane * 8);
+    else ra[buf][r - 8] = *reinterpret_cast<const bf16x8*>(base + (8 * wm + r - 8) * WIDE_FRAG + lane * 8);
   };
-  // 4 row fragments (64 rows) x 8 column fragments; skipped as a whole (one uniform branch)
-  // when all 64 rows are padding
-  auto mfma_rows = [&](int buf, int i0) {
-    if (8 * wm + i0 < nmf) {
+  // One stage (slot and register set are compile-time constants in the unrolled loop).
+  // The branches around the MFMA groups also keep the register allocator from mixing the
+  // accumulators of different groups (without them it spills).
+  auto stage = [&](int st, int slot, int buf) {
+    wait_vmcnt<8 * (WS - 2)>();
+    __builtin_amdgcn_s_waitcnt(0xc07f);        // lgkmcnt(0), vmcnt and expcnt at their maxima
+    barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    const int ld = st + WS < nst ? st + WS : nst - 1;   // clamped: a repeated stage nobody reads
 #pragma unroll
-      for (int i = i0; i < i0 + 4; ++i)
+    for (int i = 0; i < 8; ++i) {
+      if (8 * wm + i < nmf) {                  // uniform: row fragment i holds a real row
 #pragma unroll
         for (int j = 0; j < 8; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[buf][i], rb[buf][j], acc[i][j], 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (r * WIDE_READ_GROUPS / 16 == i) read_one((slot + 1) % WS, buf ^ 1, r);
+      uint16_t* base = slot_ptr(slot);
+      if (i < 4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            arsrc, (__attribute__((address_space(3))) void*)(base + (4 * wave + i) * WIDE_FRAG), 16, aoff[i],
+            ld * 64, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            brsrc, (__attribute__((address_space(3))) void*)(base + (16 + 4 * wave + i - 4) * WIDE_FRAG), 16,
+            boff[i - 4], ld * B_STAGE, 0, 0);
     }
-  };
-  // One stage; its slot and register set are compile-time constants in the unrolled loop.
-  // The middle block runs on every stage, the last ones included (they read a slot that
-  // holds a repeated stage and issue clamped loads, both unused): a branch there would
-  // merge two wait states and make the compiler wait for every LDS read before the
-  // second half.  The next stage's fragments are read before the new loads are issued.
-  auto stage = [&](int st, int slot, int buf) {
-    mfma_rows(buf, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<8 * (WS - 3)>();                // stage st+1 (8 loads per stage; st+2 .. st+WS-2 may fly)
-    barrier();
-    read((slot + 1) % WS, buf ^ 1);
-    __builtin_amdgcn_sched_barrier(0);
-    issue(st + WS - 1, (slot + WS - 1) % WS);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_rows(buf, 4);
   };
   if (nst > 0) {
 #pragma unroll
-    for (int st = 0; st < WS - 1; ++st) issue(st, st);
-    wait_vmcnt<8 * (WS - 2)>();                // stage 0
+    for (int st = 0; st < WS; ++st) issue(st, st);
+    wait_vmcnt<8 * (WS - 1)>();                // stage 0
     barrier();
-    read(0, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) read_one(0, 0, r);
     for (int base = 0;; base += UNR) {
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
@@ -746,36 +807,49 @@ __device__ __forceinline__ void ffn_gemm_wide_body(const GemmArgs& p, uint16_t* 
 wide_done:
   wait_vmcnt<0>();                             // no load into this workgroup's LDS outlives it
 
-  // ---- epilogue: C layout, lane holds rows 4 (lane / 16) + v of each 16 x 16 block, column lane % 16
+  // ---- epilogue: C layout, lane holds rows 4 (lane / 16) + v of each 16 x 16 block, column
+  // lane % 16; stored through the quad transpose (row 4 (lane / 16) + lane % 4, 4 columns
+  // from 4 ((lane / 4) % 4)).  d and F are multiples of 64, so a 16-column block is either
+  // inside the output or past it.
+  const int qrow = 4 * (lane >> 4) + (lane & 3);
+  const int qcol = 4 * ((lane >> 2) & 3);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     if (8 * wm + i >= nmf) continue;
+    const int r = 128 * wm + 16 * i + qrow;
+    const int64_t orow = ti.row_begin + r;
+    if (MODE == MODE_SWIGLU_UP) {
+      uint16_t* H = static_cast<uint16_t*>(p.out);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int r = 128 * wm + 16 * i + 4 * (lane >> 4) + v;
-      if (r >= ti.nrows) continue;
-      const int64_t orow = ti.row_begin + r;
-      if (MODE == MODE_SWIGLU_UP) {
-        uint16_t* H = static_cast<uint16_t*>(p.out);
+      for (int j = 0; j < 4; ++j) {
+        const int64_t u0 = static_cast<int64_t>(ti.ntile) * 128 + 64 * wn + 16 * j;
+        if (u0 >= p.N) continue;
+        float h[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t u = static_cast<int64_t>(ti.ntile) * 128 + 64 * wn + 16 * j + (lane & 15);
-          if (u < p.N) H[orow * p.N + u] = f32_to_bf16(silu_f(acc[i][j][v]) * acc[i][j + 4][v]);
-        }
-      } else if (MODE == MODE_GELU_UP) {
-        uint16_t* H = static_cast<uint16_t*>(p.out);
+        for (int v = 0; v < 4; ++v) h[v] = silu_f(acc[i][j][v]) * acc[i][j + 4][v];
+        const u32x2 o = quad_rows_bf16(h, lane);
+        if (r < ti.nrows) *reinterpret_cast<u32x2*>(&H[orow * p.N + u0 + qcol]) = o;
+      }
+    } else if (MODE == MODE_GELU_UP) {
+      uint16_t* H = static_cast<uint16_t*>(p.out);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int64_t c = static_cast<int64_t>(ti.ntile) * 256 + 128 * wn + 16 * j + (lane & 15);
-          if (c < p.N) H[orow * p.N + c] = f32_to_bf16(gelu_f(acc[i][j][v]));
-        }
-      } else {
-        float* Y = static_cast<float*>(p.out) + static_cast<int64_t>(ti.split) * p.split_stride;
+      for (int j = 0; j < 8; ++j) {
+        const int64_t c0 = static_cast<int64_t>(ti.ntile) * 256 + 128 * wn + 16 * j;
+        if (c0 >= p.N) continue;
+        float h[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int64_t c = static_cast<int64_t>(ti.ntile) * 256 + 128 * wn + 16 * j + (lane & 15);
-          if (c < p.N) Y[orow * p.N + c] = acc[i][j][v];
-        }
+        for (int v = 0; v < 4; ++v) h[v] = gelu_f(acc[i][j][v]);
+        const u32x2 o = quad_rows_bf16(h, lane);
+        if (r < ti.nrows) *reinterpret_cast<u32x2*>(&H[orow * p.N + c0 + qcol]) = o;
+      }
+    } else {
+      float* Y = static_cast<float*>(p.out) + static_cast<int64_t>(ti.split) * p.split_stride;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int64_t c0 = static_cast<int64_t>(ti.ntile) * 256 + 128 * wn + 16 * j;
+        if (c0 >= p.N) continue;
+        const f32x4 o = quad_rows_f32(acc[i][j], lane);
+        if (r < ti.nrows) *reinterpret_cast<f32x4*>(&Y[orow * p.N + c0 + qcol]) = o;
       }
     }
   }
