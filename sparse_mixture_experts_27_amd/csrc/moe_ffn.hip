@@ -47,13 +47,17 @@ struct SchedView {
   __device__ const int32_t* prefix() const { return base + 1; }
   __device__ const int32_t* row0() const { return base + 2 + Gt; }
   __device__ const int32_t* rows() const { return base + 2 + 2 * Gt; }
+  __device__ const int32_t* m2g() const { return base + 2 + 3 * Gt; }   // M-tile -> its group
 };
 
-inline size_t sched_words(int Gt) { return 2 + 3 * static_cast<size_t>(Gt); }
+// [total M-tiles][prefix: Gt + 1][row0: Gt][rows: Gt][group of each M-tile: max_mtiles]
+inline size_t sched_words(int Gt, int64_t max_mtiles) {
+  return 2 + 3 * static_cast<size_t>(Gt) + static_cast<size_t>(max_mtiles);
+}
 
 __global__ __launch_bounds__(1024) void ffn_schedule_kernel(const int32_t* __restrict__ offsets, int G,
                                                             int64_t max_rows, int64_t shared_rows,
-                                                            int64_t shared_row0, int bm,
+                                                            int64_t shared_row0, int bm, int64_t max_mtiles,
                                                             int32_t* __restrict__ sched) {
   __shared__ int32_t wsum[16];
   const int Gt = G + (shared_rows > 0 ? 1 : 0);
@@ -101,6 +105,13 @@ __global__ __launch_bounds__(1024) void ffn_schedule_kernel(const int32_t* __res
     prefix[Gt] = carry;
     sched[0] = carry;
   }
+  // the group of every M-tile, so a workgroup finds its group with one load (the prefix
+  // entries of other threads are visible after the loop's last barrier)
+  int32_t* m2g = sched + 2 + 3 * Gt;
+  for (int g = threadIdx.x; g < Gt; g += 1024) {
+    const int32_t end = g + 1 < Gt ? prefix[g + 1] : carry;
+    for (int32_t m = prefix[g]; m < end && m < max_mtiles; ++m) m2g[m] = g;
+  }
 }
 
 struct GemmArgs {
@@ -112,6 +123,7 @@ struct GemmArgs {
   const void* sw0;          // shared-group weights
   const void* sw1;
   const int32_t* sched;
+  int64_t max_mtiles;       // bound of the M-tile count (size of the schedule's group table)
   int G, Gt;
   int64_t shared_row0;
   int64_t K, N;             // contraction and output width (F for up, d for down)
@@ -134,21 +146,19 @@ struct TileInfo {
 __device__ __forceinline__ bool decode_tile(const GemmArgs& p, int bm, TileInfo& ti) {
   const SchedView sv{p.sched, p.Gt};
   const int64_t nts = static_cast<int64_t>(p.nt) * p.splits;
-  const int64_t n_active = static_cast<int64_t>(sv.total()) * nts;
+  // (offsets that break their contract could claim more M-tiles than the table holds)
+  const int64_t mtiles = sv.total() < p.max_mtiles ? sv.total() : p.max_mtiles;
+  const int64_t n_active = mtiles * nts;
   const int64_t per_xcd = (n_active + 7) / 8;
   const int64_t b = blockIdx.x;
   const int64_t slot = b >> 3;
   if (slot >= per_xcd) return false;
   const int64_t L = (b & 7) * per_xcd + slot;
   if (L >= n_active) return false;
-  // largest g with prefix[g] * nts <= L (prefix is non-decreasing)
+  // group g holds tiles [prefix[g] * nts, prefix[g+1] * nts), i.e. M-tiles prefix[g] ..
+  // prefix[g+1]-1 in group order: its group is one table load away
   const int32_t* pre = sv.prefix();
-  int lo = 0, hi = p.Gt;          // invariant: prefix[lo]*nts <= L < prefix[hi]*nts
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (static_cast<int64_t>(pre[mid]) * nts <= L) lo = mid; else hi = mid;
-  }
-  const int g = lo;
+  const int g = sv.m2g()[L / nts];
   // Inside a group the tiles go in blocks of up to MB M-tiles: all N-tiles (and K splits)
   // of one block, M fastest, then the next block.  The workgroups running at once on an
   // XCD then share both the weights of a few N-tiles and the activation rows of a few
@@ -1064,7 +1074,7 @@ FfnPlan ffn_plan(int64_t max_rows, int G, int64_t shared_rows, int64_t d, int64_
     while (est * nt2 * pl.splits < 256 && F / (BK * pl.splits * 2) >= 8) pl.splits *= 2;
   }
   const size_t elem = dt == MOE_BF16 ? 2 : 4;
-  size_t ws = align_up(sched_words(Gt) * sizeof(int32_t), 256);
+  size_t ws = align_up(sched_words(Gt, pl.max_mtiles) * sizeof(int32_t), 256);
   ws += align_up(static_cast<size_t>(max_rows) * F * elem, 256);                       // H
   if (pl.splits > 1) ws += align_up(static_cast<size_t>(pl.splits) * max_rows * d * 4, 256);  // partials
   pl.ws_bytes = ws;
@@ -1082,7 +1092,7 @@ moe_status_t launch_ffn(const FfnProblem& p, const FfnPlan& plan, float* y, bool
   const bool packed = p.layout == MOE_LAYOUT_PACKED;
   const int bm = plan.bm;
   WsCarver c(ws);
-  int32_t* sched = c.take<int32_t>(sched_words(Gt));
+  int32_t* sched = c.take<int32_t>(sched_words(Gt, plan.max_mtiles));
   void* H = bf ? static_cast<void*>(c.take<uint16_t>(static_cast<size_t>(p.max_rows) * p.F))
                : static_cast<void*>(c.take<float>(static_cast<size_t>(p.max_rows) * p.F));
   float* part = nullptr;
@@ -1093,7 +1103,8 @@ moe_status_t launch_ffn(const FfnProblem& p, const FfnPlan& plan, float* y, bool
   }
   if (bf && !bf16_tile_supported(bm, plan.nw)) return MOE_EINVAL;
 
-  ffn_schedule_kernel<<<1, 1024, 0, s>>>(p.offsets, p.G, p.max_rows, p.shared_rows, p.shared_row0, bm, sched);
+  ffn_schedule_kernel<<<1, 1024, 0, s>>>(p.offsets, p.G, p.max_rows, p.shared_rows, p.shared_row0, bm,
+                                         plan.max_mtiles, sched);
   if (moe_status_t st = check_launch("ffn schedule kernel")) return st;
   mark(0);
 
@@ -1101,6 +1112,7 @@ moe_status_t launch_ffn(const FfnProblem& p, const FfnPlan& plan, float* y, bool
   g.perm = p.perm;
   g.k_div = p.k > 0 ? p.k : 1;
   g.sched = sched;
+  g.max_mtiles = plan.max_mtiles;
   g.G = p.G;
   g.Gt = Gt;
   g.shared_row0 = p.shared_row0;
