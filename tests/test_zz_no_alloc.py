@@ -71,3 +71,41 @@ def test_noalloc_matches_workspace_entry_point(name):
             lin = synth.make_inputs(cfg, DEV)             # the oracle reads the nn.Linear layout
             check_output(sub, x64, z_o, res, expert_fetcher(cfg, lin), shared_weights(lin), None, rep)
             say(f"[ok] no-alloc vs oracle: {rep}")
+
+
+def _packed(cfg):
+    inp = synth.make_inputs(cfg, DEV)
+    for n in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down"):
+        if inp[n] is not None:
+            inp[n] = B.pack_weights(inp[n])
+    return inp
+
+
+def test_noalloc_graph_replay():
+    """The fixed-scratch entry point captured in a HIP graph (the callers it is for): every
+    replay, with a new input copied into the captured buffer and another layer's
+    fixed-scratch calls in between (they overwrite the shared scratch), gives the bits of
+    the workspace entry point on the same input."""
+    cfg = CASES["bf16-decode"]
+    inp = _packed(cfg)
+    Lw, Ln = _layer(cfg, inp, False), _layer(cfg, inp, True)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(cfg.seed + 1)
+    xs = [inp["x"], torch.randn(inp["x"].shape, generator=gen, device=DEV).to(inp["x"].dtype)]
+    ref = [Lw(x).clone() for x in xs]
+    _ = Ln(xs[0])                                    # first call on the device, outside the capture
+    x_static = xs[0].clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = Ln(x_static)
+    ocfg = CASES["bf16-shared-capacity-reroute"]
+    oinp = _packed(ocfg)
+    Lo = _layer(ocfg, oinp, True)
+    for i in (1, 0, 1, 1, 0):
+        x_static.copy_(xs[i])
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"[case] no-alloc graph replay {cfg.label} input {i}")
+        assert torch.equal(out.view(torch.int32), ref[i].view(torch.int32)), i
+        _ = Lo(oinp["x"]).sum().item()
