@@ -60,26 +60,42 @@
 extern "C" {
 #endif
 
+/* Every enum below also lists a smallest and a largest int32 value (the *_RANGE_MIN_ and
+ * *_RANGE_MAX_ entries, never valid arguments): every int a C caller passes is then a value
+ * of the type, and the library can reject an out-of-range one with MOE_EINVAL (in C++ an
+ * enum object may not hold a value outside the range of its enumerators). */
 typedef enum {
+  MOE_STATUS_RANGE_MIN_ = -2147483647 - 1,
   MOE_OK = 0,
   MOE_EINVAL = 1,        /* null required pointer, bad size or enum */
   MOE_EUNSUPPORTED = 2,  /* valid but unsupported shape (e.g. bf16 d % 64 != 0) */
   MOE_EWORKSPACE = 3,    /* workspace smaller than the *_workspace_bytes() figure */
-  MOE_EHIP = 4           /* a HIP launch or runtime call failed */
+  MOE_EHIP = 4,          /* a HIP launch or runtime call failed */
+  MOE_STATUS_RANGE_MAX_ = 2147483647
 } moe_status_t;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
-typedef enum { MOE_ACT_GELU = 0, MOE_ACT_SWIGLU = 1 } moe_act_t;
+typedef enum { MOE_DTYPE_RANGE_MIN_ = -2147483647 - 1, MOE_F32 = 0, MOE_BF16 = 1, MOE_DTYPE_RANGE_MAX_ = 2147483647 } moe_dtype_t;
+typedef enum { MOE_ACT_RANGE_MIN_ = -2147483647 - 1, MOE_ACT_GELU = 0, MOE_ACT_SWIGLU = 1, MOE_ACT_RANGE_MAX_ = 2147483647 } moe_act_t;
 /* Routing weights of the selected experts:
  *   MOE_WEIGHTS_RENORMALIZED  w_j = p_{s_j} / sum_{i<k} p_{s_i}   ([mlqm] §3.3, §4.2)
  *   MOE_WEIGHTS_SOFTMAX       w_j = p_{s_j}, the softmax probabilities themselves
  *                             ("MoE混合专家架构原理与工程实践…" §3.2: output = p1 e1 + p2 e2) */
-typedef enum { MOE_WEIGHTS_RENORMALIZED = 0, MOE_WEIGHTS_SOFTMAX = 1 } moe_weights_t;
+typedef enum {
+  MOE_WEIGHTS_RANGE_MIN_ = -2147483647 - 1,
+  MOE_WEIGHTS_RENORMALIZED = 0,
+  MOE_WEIGHTS_SOFTMAX = 1,
+  MOE_WEIGHTS_RANGE_MAX_ = 2147483647
+} moe_weights_t;
 /* Order in which slots claim expert capacity ([rkmt] §2.3 keeps what fits, drops the rest):
  *   MOE_PRIORITY_TOKEN  ascending token, then slot: the earliest tokens are kept
  *   MOE_PRIORITY_SLOT   all first choices, then all second choices, ...; ascending token
  *                       within one slot position (first choices are never displaced) */
-typedef enum { MOE_PRIORITY_TOKEN = 0, MOE_PRIORITY_SLOT = 1 } moe_priority_t;
+typedef enum {
+  MOE_PRIORITY_RANGE_MIN_ = -2147483647 - 1,
+  MOE_PRIORITY_TOKEN = 0,
+  MOE_PRIORITY_SLOT = 1,
+  MOE_PRIORITY_RANGE_MAX_ = 2147483647
+} moe_priority_t;
 /* What happens to a slot beyond its expert's capacity ([rkmt] §2.3: dropped, or sent to
  * the next-best expert):
  *   MOE_OVERFLOW_DROP     the slot contributes zero
@@ -88,14 +104,24 @@ typedef enum { MOE_PRIORITY_TOKEN = 0, MOE_PRIORITY_SLOT = 1 } moe_priority_t;
  *                         (by logit, lowest index on ties) outside its top-k and its
  *                         earlier re-routes that still has room, else are dropped; a moved
  *                         slot keeps its routing weight */
-typedef enum { MOE_OVERFLOW_DROP = 0, MOE_OVERFLOW_REROUTE = 1 } moe_overflow_t;
+typedef enum {
+  MOE_OVERFLOW_RANGE_MIN_ = -2147483647 - 1,
+  MOE_OVERFLOW_DROP = 0,
+  MOE_OVERFLOW_REROUTE = 1,
+  MOE_OVERFLOW_RANGE_MAX_ = 2147483647
+} moe_overflow_t;
 /* Storage order of the bf16 expert weights (w_gate, w_up, w_down and the shared expert's):
  *   MOE_LAYOUT_LINEAR  the nn.Linear layout [G, N, K], K contiguous
  *   MOE_LAYOUT_PACKED  the same values reordered by moe_pack_weights into MFMA operand
  *                      fragments (same size); the expert FFN then reads each 16 x 32
  *                      fragment as one contiguous KiB.  The results are bit-identical to
  *                      the linear layout's. */
-typedef enum { MOE_LAYOUT_LINEAR = 0, MOE_LAYOUT_PACKED = 1 } moe_layout_t;
+typedef enum {
+  MOE_LAYOUT_RANGE_MIN_ = -2147483647 - 1,
+  MOE_LAYOUT_LINEAR = 0,
+  MOE_LAYOUT_PACKED = 1,
+  MOE_LAYOUT_RANGE_MAX_ = 2147483647
+} moe_layout_t;
 
 /* Explicit tile shape of the bf16 grouped expert GEMM (host struct; for tuning and tests).
  *   rows   rows per M-tile: 32, 64, 128, 192 or 256; 0 = chosen from the sizes (the

@@ -147,6 +147,7 @@ const char* moe_status_string(moe_status_t s) {
     case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: unsupported shape";
     case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace too small";
     case MOE_EHIP: return "MOE_EHIP: HIP runtime error";
+    default: break;
   }
   return "unknown moe_status_t";
 }

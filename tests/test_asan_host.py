@@ -1,12 +1,13 @@
-"""The C ABI's host code under AddressSanitizer (no GPU needed).
+"""The C ABI's host code under AddressSanitizer and UndefinedBehaviorSanitizer (no GPU needed).
 
-Every library source is compiled with AddressSanitizer on the host side only (device
-code unchanged), a small C++ driver (tests/asan_abi_driver.cpp) is linked against the
+Every library source is compiled with both sanitizers on the host side only (device
+code unchanged; undefined behaviour aborts), a small C++ driver (tests/asan_abi_driver.cpp) is linked against the
 objects, and the driver exercises every host-only path of the ABI: argument validation
 of each entry point, workspace and plan queries, the capacity rule, status strings and
 the per-thread error message (including a message longer than its buffer and eight host
 threads failing at once).  None of these calls touches a GPU.  An invalid host memory
-access in the library aborts the driver with an AddressSanitizer report.
+access, or undefined behaviour such as a signed overflow in a size computation, aborts
+the driver with a sanitizer report.
 """
 import concurrent.futures as cf
 import glob
@@ -28,7 +29,7 @@ def _run(cmd):
     return r
 
 
-def test_abi_host_code_under_asan():
+def test_abi_host_code_under_sanitizers():
     if not os.path.exists(HIPCC) or not shutil.which("g++"):
         pytest.skip("hipcc or g++ not available")
     os.makedirs(OUT, exist_ok=True)
@@ -38,20 +39,26 @@ def test_abi_host_code_under_asan():
         obj = os.path.join(OUT, os.path.basename(src) + ".o")
         _run([HIPCC, "-O2", "-g", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-I", inc,
               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-              "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer",
+              "-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-sanitize-recover=undefined",
+              # checks whose runtime handlers the GNU sanitizer runtime the link uses lacks
+              "-Xarch_host", "-fno-sanitize=function,vptr",
+              "-Xarch_host", "-fno-omit-frame-pointer",
               "-c", src, "-o", obj])
         return obj
 
     with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
         objs = list(ex.map(compile_hip, sorted(glob.glob(os.path.join(CSRC, "*.hip")))))
     drv_obj = os.path.join(OUT, "asan_abi_driver.o")
-    _run(["g++", "-O1", "-g", "-std=c++17", "-fsanitize=address", "-fno-omit-frame-pointer",
+    _run(["g++", "-O1", "-g", "-std=c++17", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+          "-fno-omit-frame-pointer",
           "-D__HIP_PLATFORM_AMD__", "-I", inc, "-I", "/opt/rocm/include",
           "-c", os.path.join(ROOT, "tests", "asan_abi_driver.cpp"), "-o", drv_obj])
     exe = os.path.join(OUT, "asan_abi_driver")
-    _run(["g++", "-fsanitize=address", drv_obj, *objs, "-L/opt/rocm/lib", "-lamdhip64",
+    _run(["g++", "-fsanitize=address,undefined", drv_obj, *objs, "-L/opt/rocm/lib", "-lamdhip64",
           "-Wl,-rpath,/opt/rocm/lib", "-pthread", "-o", exe])
-    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1")
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
     r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=120)
-    assert r.returncode == 0 and "AddressSanitizer" not in r.stderr, r.stdout[-2000:] + r.stderr[-4000:]
+    assert r.returncode == 0 and "Sanitizer" not in r.stderr and "runtime error" not in r.stderr, \
+        r.stdout[-2000:] + r.stderr[-4000:]
     assert "all checks passed" in r.stdout
